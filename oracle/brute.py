@@ -1,0 +1,88 @@
+"""50-digit scalar brute force over the literal definitions (tiny inputs only).
+
+Test infrastructure only. These loops share nothing with ``reference``: they
+decode bits themselves, walk the block table themselves and never subtract a
+running maximum, so a slip in the f64 oracle's gather, scaling, softmax or
+LSE shows up as a disagreement.
+"""
+from __future__ import annotations
+
+import struct
+
+import mpmath
+
+mpmath.mp.dps = 50
+
+
+def _bits_to_mpf(bits: int, dtype: str):
+    bits = int(bits)
+    if dtype == "f16":
+        sign = -1 if bits >> 15 else 1
+        e = (bits >> 10) & 0x1F
+        f = bits & 0x3FF
+        if e == 0:
+            return sign * mpmath.mpf(f) * mpmath.mpf(2) ** -24
+        if e == 31:
+            raise ValueError("non-finite input")
+        return sign * (1 + mpmath.mpf(f) / 1024) * mpmath.mpf(2) ** (e - 15)
+    if dtype == "bf16":
+        val = struct.unpack("<f", struct.pack("<I", bits << 16))[0]
+        return mpmath.mpf(val)
+    raise ValueError(dtype)
+
+
+def _row(pool, phys, slot, dtype):
+    return [_bits_to_mpf(v, dtype) for v in pool[phys][slot]]
+
+
+def latent_brute(case, b: int, h: int):
+    """out[b, h] (list of 512 mpf) and lse2[b, h] (mpf) by the definition."""
+    n = int(case.context_lens[b])
+    qa = [_bits_to_mpf(v, case.dtype) for v in case.q_absorbed[b][h]]
+    qp = [_bits_to_mpf(v, case.dtype) for v in case.q_pe[b][h]]
+    scale = mpmath.mpf(case.scale)
+    num = [mpmath.mpf(0)] * len(qa)
+    den = mpmath.mpf(0)
+    for t in range(n):
+        phys = int(case.block_table[b][t // 32])
+        c = _row(case.ckv_pool, phys, t % 32, case.dtype)
+        k = _row(case.kpe_pool, phys, t % 32, case.dtype)
+        s = scale * (mpmath.fsum(x * y for x, y in zip(qa, c))
+                     + mpmath.fsum(x * y for x, y in zip(qp, k)))
+        e = mpmath.exp(s)
+        den += e
+        for i in range(len(num)):
+            num[i] += e * c[i]
+    if n == 0:
+        return [mpmath.mpf(0)] * len(qa), mpmath.mpf("-inf")
+    return [x / den for x in num], mpmath.log(den) / mpmath.log(2)
+
+
+def decompressed_brute(case, b: int, h: int, q_nope, W_UK, W_UV_T):
+    """Pre-absorption attention for one (b, h) by the definition.
+
+    q_nope [dn] floats; W_UK [dn, 512]; W_UV_T [512, dv] (plain floats).
+    """
+    n = int(case.context_lens[b])
+    qn = [mpmath.mpf(float(x)) for x in q_nope]
+    qp = [_bits_to_mpf(v, case.dtype) for v in case.q_pe[b][h]]
+    scale = mpmath.mpf(case.scale)
+    dn = len(qn)
+    dv = len(W_UV_T[0])
+    num = [mpmath.mpf(0)] * dv
+    den = mpmath.mpf(0)
+    for t in range(n):
+        phys = int(case.block_table[b][t // 32])
+        c = _row(case.ckv_pool, phys, t % 32, case.dtype)
+        k = _row(case.kpe_pool, phys, t % 32, case.dtype)
+        key = [mpmath.fsum(mpmath.mpf(float(W_UK[d][i])) * c[i] for i in range(len(c)))
+               for d in range(dn)]
+        val = [mpmath.fsum(c[i] * mpmath.mpf(float(W_UV_T[i][j])) for i in range(len(c)))
+               for j in range(dv)]
+        s = scale * (mpmath.fsum(x * y for x, y in zip(qn, key))
+                     + mpmath.fsum(x * y for x, y in zip(qp, k)))
+        e = mpmath.exp(s)
+        den += e
+        for j in range(dv):
+            num[j] += e * val[j]
+    return [x / den for x in num], mpmath.log(den) / mpmath.log(2)

@@ -1,0 +1,371 @@
+"""Pins of the f64 oracle against things other than itself (CPU only).
+
+Each test names the passage it follows. Pins used: 50-digit brute force,
+closed forms (one token, uniform scores), needles, layout invariance,
+split/merge invariance, the absorption identity, the log2-vs-ln negative
+control, and the pages' printed byte counts. A last test plants plausible
+mistakes in a copy of the oracle and checks that some pin catches each.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import mla_synth
+import oracle
+from oracle import brute, reference
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def small_case(seed, contexts, heads=2, dtype="f16", **kw):
+    return mla_synth.make_case(seed=seed, batch=len(contexts), heads=heads,
+                               contexts=contexts, dtype=dtype, **kw)
+
+
+def _brute_errors(case, b, h, out, lse2):
+    bo, bl = brute.latent_brute(case, b, h)
+    bo = np.array([float(x) for x in bo])
+    return np.max(np.abs(out[b, h] - bo)), abs(lse2[b, h] - float(bl))
+
+
+# --- P7: brute force on tiny inputs --------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("contexts", [[1], [31], [32, 33], [70, 5]])
+def test_latent_matches_brute_force(dtype, contexts):
+    # mlxcel pull request 995, "What changed", Stage 1: score
+    # scale*(q_abs.ckv + q_pe.kpe), values ckv, softmax over the context.
+    case = small_case(11 + len(contexts) + contexts[0], contexts, dtype=dtype,
+                      poison=True)
+    out, lse2 = oracle.latent_f64(case)
+    for b in range(case.batch):
+        for h in range(case.heads):
+            eo, el = _brute_errors(case, b, h, out, lse2)
+            assert eo < 1e-12 and el < 1e-12, (b, h, eo, el)
+
+
+def test_decompressed_matches_brute_force():
+    # mlxcel pull request 995, "Verified vs unverified": a host f64 reference
+    # that performs the pre-absorption computation. Small nope/value widths
+    # keep the 50-digit loops short; the identity does not depend on them.
+    case = small_case(21, [37], heads=2, dtype="bf16")
+    rng = np.random.default_rng(5)
+    dn, dv = 8, 6
+    q_nope = rng.standard_normal((1, 2, dn))
+    W_UK = rng.standard_normal((2, dn, 512)) / 16
+    W_UV_T = rng.standard_normal((2, 512, dv)) / 16
+    o, l = oracle.decompressed_f64(case, q_nope, W_UK, W_UV_T)
+    for h in range(2):
+        bo, bl = brute.decompressed_brute(case, 0, h, q_nope[0, h], W_UK[h], W_UV_T[h])
+        assert np.max(np.abs(o[0, h] - np.array([float(x) for x in bo]))) < 1e-12
+        assert abs(l[0, h] - float(bl)) < 1e-12
+
+
+# --- P8: the absorption identity ------------------------------------------
+
+@pytest.mark.parametrize("contexts,heads", [([45], 2), ([300, 1], 4)])
+def test_absorption_identity(contexts, heads):
+    # mlxcel pull request 995, "What changed", absorb.rs: q_nope.(W_UK ckv) =
+    # (q_nope W_UK).ckv and o = (sum p ckv) W_UV^T, so the latent path through
+    # the folded weights equals the decompressed path (DeepSeek geometry:
+    # qk_nope = v_head = 128).
+    case = small_case(31 + heads, contexts, heads=heads, dtype="f16")
+    rng = np.random.default_rng(7)
+    q_nope = rng.standard_normal((case.batch, heads, 128))
+    W_UK = rng.standard_normal((heads, 128, 512)) / 22
+    W_UV_T = rng.standard_normal((heads, 512, 128)) / 22
+    o_dec, l_dec = oracle.decompressed_f64(case, q_nope, W_UK, W_UV_T)
+    qa = oracle.absorb_query(q_nope, W_UK)
+    qp = reference.decode16(case.q_pe, case.dtype)
+    for b in range(case.batch):
+        C, Kp = oracle.gather_request(case.ckv_pool, case.kpe_pool, case.block_table[b],
+                                      int(case.context_lens[b]), case.dtype)
+        o_lat, l_lat = reference._attend(qa[b], qp[b], C, Kp, case.scale)
+        o_back = oracle.unabsorb_output(o_lat[None], W_UV_T)[0]
+        assert np.max(np.abs(o_back - o_dec[b])) < 1e-12
+        assert np.max(np.abs(l_lat - l_dec[b])) < 1e-12
+
+
+def test_square_orthogonal_pre_absorption_mode():
+    # With square orthogonal folds the pre-absorption path runs at the full
+    # 512-wide latent and maps back by a transpose; it must equal latent_f64.
+    case = small_case(41, [777, 64], heads=3, dtype="bf16")
+    W_UK, W_UV_T = oracle.orthogonal_weights(99, case.heads)
+    qa = reference.decode16(case.q_absorbed, case.dtype)
+    q_nope = np.einsum("bhr,hdr->bhd", qa, W_UK)          # q_abs W_UK^T
+    o, l = oracle.decompressed_f64(case, q_nope, W_UK, W_UV_T)
+    o_lat = np.einsum("bhv,hrv->bhr", o, W_UV_T)           # o (W_UV^T)^T
+    ref, lref = oracle.latent_f64(case)
+    assert np.max(np.abs(o_lat - ref)) < 1e-11
+    assert np.max(np.abs(l - lref)) < 1e-11
+
+
+# --- P1 / P2: closed forms ------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_single_token_closed_form(dtype):
+    # One visible token: its weight is exactly 1, out = ckv_0, and
+    # lse2 = s_0 / ln 2.
+    case = small_case(51, [1, 1], heads=4, dtype=dtype, poison=True)
+    out, lse2 = oracle.latent_f64(case)
+    for b in range(2):
+        phys = case.block_table[b, 0]
+        c = reference.decode16(case.ckv_pool[phys, 0], dtype)
+        k = reference.decode16(case.kpe_pool[phys, 0], dtype)
+        for h in range(4):
+            assert np.array_equal(out[b, h], c)
+            qa = reference.decode16(case.q_absorbed[b, h], dtype)
+            qp = reference.decode16(case.q_pe[b, h], dtype)
+            s0 = case.scale * (math.fsum(qa * c) + math.fsum(qp * k))
+            assert abs(lse2[b, h] - s0 * oracle.LOG2_E) < 1e-13
+
+
+@pytest.mark.parametrize("n", [1, 2, 31, 32, 33, 64, 100, 1024])
+def test_uniform_scores_closed_form(n):
+    # q = 0 makes every score 0: out is the plain mean of the visible rows
+    # and lse2 = log2 n. Exactly which rows are read shows in the mean.
+    case = small_case(61 + n, [n], heads=2, dtype="bf16", poison=True)
+    case.q_absorbed[:] = 0
+    case.q_pe[:] = 0
+    out, lse2 = oracle.latent_f64(case)
+    rows = np.stack([reference.decode16(case.ckv_pool[case.block_table[0, t // 32], t % 32],
+                                        "bf16") for t in range(n)])
+    mean = rows.sum(axis=0) / n
+    assert np.max(np.abs(out[0] - mean[None])) < 1e-13
+    assert np.all(np.abs(lse2[0] - math.log2(n)) < 1e-13)
+    if n & (n - 1) == 0:
+        assert np.all(lse2[0] == math.log2(n))
+
+
+def test_empty_context():
+    # No visible token: zero output and lse2 = -inf, never NaN (MTPLX pull
+    # request 639, commit on rows without a visible key).
+    case = small_case(71, [0, 40], heads=2)
+    out, lse2 = oracle.latent_f64(case)
+    assert np.all(out[0] == 0) and np.all(lse2[0] == -np.inf)
+    assert np.all(np.isfinite(out[1])) and np.all(np.isfinite(lse2[1]))
+
+
+# --- P3: needles ----------------------------------------------------------
+
+def plant_needle(case, b, t, h):
+    """Make token t of request b dominate head h's softmax (out ~= its row)."""
+    phys = case.block_table[b, t // 32] if t // 32 < case.block_table.shape[1] else None
+    sign = np.sign(reference.decode16(case.q_absorbed[b, h], case.dtype))
+    sign[sign == 0] = 1
+    row = (6.0 * sign).astype(np.float32)
+    case.ckv_pool[phys, t % 32] = mla_synth.encode16(row, case.dtype)
+    case.kpe_pool[phys, t % 32] = mla_synth.encode16(np.zeros(64, np.float32), case.dtype)
+    return reference.decode16(case.ckv_pool[phys, t % 32], case.dtype)
+
+
+@pytest.mark.parametrize("t", [0, 31, 32, 63, 64, 150, 199])
+def test_needle_is_found(t):
+    case = small_case(81, [200], heads=2)
+    needle = plant_needle(case, 0, t, 1)
+    out, _ = oracle.latent_f64(case)
+    assert np.max(np.abs(out[0, 1] - needle)) < 1e-12
+
+
+@pytest.mark.parametrize("t", [200, 223])
+def test_needle_past_context_end_is_ignored(t):
+    # Rows past the context end in the last block must not be read.
+    case = small_case(82, [200], heads=2)
+    before, _ = oracle.latent_f64(case)
+    plant_needle(case, 0, t, 1)
+    after, _ = oracle.latent_f64(case)
+    assert np.array_equal(before, after)
+
+
+# --- P4: layout invariance --------------------------------------------------
+
+def test_block_permutation_invariance():
+    # Only logical token order matters: permuting the physical pool and
+    # rewriting the table leaves the answer bit-identical.
+    case = small_case(91, [150, 65], heads=3, dtype="bf16")
+    out, lse2 = oracle.latent_f64(case)
+    rng = np.random.default_rng(3)
+    perm = rng.permutation(case.num_blocks)          # new position of block i
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(perm.size)
+    case.ckv_pool = case.ckv_pool[inv]
+    case.kpe_pool = case.kpe_pool[inv]
+    case.block_table = perm[case.block_table].astype(np.int32)
+    out2, lse22 = oracle.latent_f64(case)
+    assert np.array_equal(out, out2) and np.array_equal(lse2, lse22)
+
+
+# --- P5: split / merge invariance --------------------------------------------
+
+@pytest.mark.parametrize("contexts", [[1000], [1024], [33, 97, 1]])
+def test_split_merge_equals_single_pass(contexts):
+    # vllm-metal pull request 601, "What changed": the LSE-weighted reduce of
+    # slices gives the single-pass answer; mlxcel pull request 995, "How
+    # #898's merge kernel is reused": the split matches at every chunk
+    # length and the merge is associative across regroupings.
+    case = small_case(101 + len(contexts), contexts, heads=2)
+    ref, lref = oracle.latent_f64(case)
+    for P in range(1, 9):
+        for S in (1, 2, 3, 7):
+            Ps = [P] * case.batch
+            Ss = [S] * case.batch
+            ranges = oracle.row_ranges(case.context_lens, Ps, Ss)
+            indptr = np.concatenate([[0], np.cumsum([p * s for p, s in zip(Ps, Ss)])])
+            po, pl = oracle.partials_f64(case, ranges, indptr)
+            out, lse2 = oracle.merge_log2_f64(po, pl, indptr)
+            assert np.max(np.abs(out - ref)) < 1e-13, (P, S)
+            assert np.max(np.abs(lse2 - lref)) < 1e-12, (P, S)
+
+
+def test_merge_regrouping_is_associative():
+    # Merging rows in two stages (pairs first) equals merging all at once.
+    case = small_case(111, [900], heads=2)
+    ranges = oracle.row_ranges(case.context_lens, [8], [1])
+    po, pl = oracle.partials_f64(case, ranges, [0, 8])
+    one, l_one = oracle.merge_log2_f64(po, pl, [0, 8])
+    pairs, l_pairs = oracle.merge_log2_f64(po, pl, [0, 2, 4, 6, 8])
+    two, l_two = oracle.merge_log2_f64(pairs.reshape(4, 2, 512), l_pairs.reshape(4, 2), [0, 4])
+    assert np.max(np.abs(one - two)) < 1e-14
+    assert np.max(np.abs(l_one - l_two)) < 1e-13
+
+
+def test_merge_of_empty_rows_gives_zero_not_nan():
+    po = np.zeros((3, 2, 512))
+    pl = np.full((3, 2), -np.inf)
+    out, lse2 = oracle.merge_log2_f64(po, pl, [0, 3])
+    assert np.all(out == 0) and np.all(lse2 == -np.inf)
+
+
+# --- P6: negative control ----------------------------------------------------
+
+def test_natural_log_lse_gives_wrong_answer():
+    # mlxcel pull request 995, "How #898's merge kernel is reused": a
+    # natural-log LSE fed to the log2 merge still returns a plausible but
+    # wrong weighted average. The control needs partition LSEs a few units
+    # apart (equal ones weight rows alike under both conventions; a dominant
+    # needle makes both pick the same row), so partition 0's latent rows are
+    # scaled by 1.5.
+    case = small_case(121, [1024], heads=2)
+    blocks = case.block_table[0, :8]
+    hot = reference.decode16(case.ckv_pool[blocks], case.dtype) * 1.5
+    case.ckv_pool[blocks] = mla_synth.encode16(hot.astype(np.float32), case.dtype)
+    ref, _ = oracle.latent_f64(case)
+    ranges = oracle.row_ranges(case.context_lens, [4], [1])
+    po, pl = oracle.partials_f64(case, ranges, [0, 4])
+    good, _ = oracle.merge_log2_f64(po, pl, [0, 4])
+    bad, _ = oracle.merge_ln_wrong(po, pl, [0, 4])
+    assert np.max(np.abs(good - ref)) < 1e-13
+    assert np.max(np.abs(bad - ref)) > 10 * 1e-2
+    assert np.all(np.isfinite(bad))
+
+
+def test_negative_control_needs_unequal_lses():
+    # With equal LSEs both conventions weight rows equally, which is why the
+    # control above builds unequal ones.
+    po = np.random.default_rng(0).standard_normal((4, 1, 512))
+    pl = np.full((4, 1), 3.0)
+    good, _ = oracle.merge_log2_f64(po, pl, [0, 4])
+    bad, _ = oracle.merge_ln_wrong(po, pl, [0, 4])
+    assert np.max(np.abs(good - bad)) < 1e-15
+
+
+# --- P10: the pages' printed byte counts -------------------------------------
+
+def test_byte_model_matches_printed_numbers():
+    with open(os.path.join(GOLDEN, "kv_byte_model.json")) as f:
+        g = json.load(f)
+    geo, printed = g["geometry"], g["printed"]
+    lat = oracle.latent_bytes_per_token(geo["elem_bytes"], geo["latent"], geo["rope"])
+    dec = oracle.decompressed_bytes_per_token(geo["heads"], geo["qk_head_dim"],
+                                              geo["v_head_dim"], geo["elem_bytes"])
+    assert lat == 1152 and dec == 10240
+    assert round(dec / lat, 2) == printed["ratio_rounded_2dp"]
+    budget = printed["budget_bytes"]
+    assert budget == 16 * 2 ** 30
+    assert oracle.max_context_tokens(budget, dec, geo["layers"]) == printed["max_tokens_decompressed"]
+    assert oracle.max_context_tokens(budget, lat, geo["layers"]) == printed["max_tokens_latent"]
+
+
+# --- the generator's rounding ------------------------------------------------
+
+def test_bf16_encoder_rounds_to_nearest_even():
+    # Ties go to the even neighbour; everything else to the nearer one.
+    vals = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -8 + 2 ** -20,
+                     -1.0 - 2 ** -8, 3.0e-39, 65504.0], dtype=np.float32)
+    bits = mla_synth.f32_to_bf16_bits(vals)
+    back = reference.decode16(bits, "bf16")
+    expect = [1.0, 1.0, 1.0 + 2 * 2 ** -7, 1.0 + 2 ** -7, -1.0]
+    assert list(back[:5]) == expect
+    for v, r in zip(vals, back):
+        # brute force: r is a nearest representable neighbour of v
+        lo = reference.decode16(np.uint16(np.float32(v).view(np.uint32) >> 16), "bf16")
+        hi_bits = (np.float32(v).view(np.uint32) >> 16) + 1
+        hi = reference.decode16(np.uint16(hi_bits), "bf16")
+        assert abs(r - v) <= min(abs(lo - v), abs(hi - v))
+
+
+# --- planted mistakes: every one must trip a pin ------------------------------
+
+def _pins_pass(case_b):
+    """Run a quick brute-force + closed-form check; True if all agree."""
+    out, lse2 = oracle.latent_f64(case_b)
+    for b in range(case_b.batch):
+        for h in range(case_b.heads):
+            eo, el = _brute_errors(case_b, b, h, out, lse2)
+            if not (eo < 1e-12 and el < 1e-12):
+                return False
+    return True
+
+
+def _mutant_attend_no_rope(qa, qp, C, Kp, scale):
+    return ORIG_ATTEND(qa, np.zeros_like(qp), C, Kp, scale)
+
+
+def _mutant_attend_ln_lse(qa, qp, C, Kp, scale):
+    o, l = ORIG_ATTEND(qa, qp, C, Kp, scale)
+    return o, l * reference.LN_2
+
+
+def _mutant_attend_scale_twice(qa, qp, C, Kp, scale):
+    return ORIG_ATTEND(qa, qp, C, Kp, scale * scale)
+
+
+def _mutant_attend_sign(qa, qp, C, Kp, scale):
+    return ORIG_ATTEND(-qa, -qp, C, Kp, scale)
+
+
+def _mutant_gather_off_by_one(ckv_pool, kpe_pool, table_row, n, dtype, lo=0, hi=None):
+    hi = n if hi is None else min(hi, n)
+    t = np.arange(max(0, lo), hi)
+    phys = np.asarray(table_row)[(t + 1) // 32]
+    slot = (t + 1) % 32
+    return (reference.decode16(ckv_pool[phys, slot], dtype),
+            reference.decode16(kpe_pool[phys, slot], dtype))
+
+
+def _mutant_gather_drop_last(ckv_pool, kpe_pool, table_row, n, dtype, lo=0, hi=None):
+    return ORIG_GATHER(ckv_pool, kpe_pool, table_row, max(0, n - 1), dtype, lo, hi)
+
+
+ORIG_ATTEND = reference._attend
+ORIG_GATHER = reference.gather_request
+
+
+@pytest.mark.parametrize("mutant", ["no_rope", "ln_lse", "scale_twice", "sign",
+                                    "gather_off_by_one", "gather_drop_last"])
+def test_planted_mistakes_are_caught(monkeypatch, mutant):
+    case = small_case(131, [40], heads=1, dtype="f16")
+    assert _pins_pass(case)
+    if mutant.startswith("gather"):
+        fn = {"gather_off_by_one": _mutant_gather_off_by_one,
+              "gather_drop_last": _mutant_gather_drop_last}[mutant]
+        monkeypatch.setattr(reference, "gather_request", fn)
+    else:
+        fn = {"no_rope": _mutant_attend_no_rope, "ln_lse": _mutant_attend_ln_lse,
+              "scale_twice": _mutant_attend_scale_twice,
+              "sign": _mutant_attend_sign}[mutant]
+        monkeypatch.setattr(reference, "_attend", fn)
+    assert not _pins_pass(case)
