@@ -1,0 +1,271 @@
+"""Python binding of libmla_decode.so: split-KV, matrix-absorbed MLA decode
+over a paged latent KV cache on MI355X (gfx950).
+
+The functions here carry the C ABI's names (include/mla_decode.h) and only
+marshal arguments: every step of the decode runs in the HIP kernels of the
+library. torch is used for device memory and the current stream. If the
+library is not built, importing works but every call raises; build it with
+``python -m absorbed_mla_paged_amd._build`` (or ``__graft_entry__.build()``).
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmla_decode.so")
+
+MLA_F16, MLA_BF16 = 0, 1
+KV_LORA_RANK, ROPE_DIM, BLOCK_SIZE = 512, 64, 32
+STATUS = {0: "MLA_OK", -1: "MLA_E_NULL", -2: "MLA_E_SHAPE", -3: "MLA_E_RANGE",
+          -4: "MLA_E_ALIGN", -5: "MLA_E_WORKSPACE", -6: "MLA_E_UNSUPPORTED",
+          -7: "MLA_E_HIP"}
+
+# Every function include/mla_decode.h declares.
+EXPORTS = ["mla_default_plan_params", "mla_choose_partitions", "mla_partition_range",
+           "mla_decode_partition", "mla_decode_reduce", "mla_status_string",
+           "mla_last_error", "mla_get_counters", "mla_reset_counters"]
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class _PlanParams(ctypes.Structure):
+    _fields_ = [("min_split_ctx", ctypes.c_int32), ("tokens_per_partition", ctypes.c_int32),
+                ("min_partitions", ctypes.c_int32), ("max_partitions", ctypes.c_int32),
+                ("num_cus", ctypes.c_int32), ("heads_per_wg", ctypes.c_int32),
+                ("min_tile_blocks", ctypes.c_int32), ("wgs_per_cu", ctypes.c_int32),
+                ("force_partitions", ctypes.c_int32), ("force_splits", ctypes.c_int32),
+                ("workspace_limit_bytes", ctypes.c_int64)]
+
+
+class _PlanInfo(ctypes.Structure):
+    _fields_ = [("total_rows", ctypes.c_int32), ("max_rows_per_req", ctypes.c_int32),
+                ("heads_per_wg", ctypes.c_int32), ("groups", ctypes.c_int32),
+                ("tile_blocks", ctypes.c_int32), ("needs_reduce", ctypes.c_int32),
+                ("partial_out_bytes", ctypes.c_int64), ("partial_lse_bytes", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load_library(path: str | None = None):
+    """Load (once) and return the ctypes handle; raise if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise MlaError(-7, f"{path} is not built; run python -m absorbed_mla_paged_amd._build")
+    lib = ctypes.CDLL(path, mode=ctypes.RTLD_LOCAL)
+    i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    pi32 = ctypes.POINTER(ctypes.c_int32)
+    lib.mla_default_plan_params.argtypes = [ctypes.POINTER(_PlanParams)]
+    lib.mla_default_plan_params.restype = None
+    lib.mla_choose_partitions.argtypes = [i32, i32, i32, pi32, i32, ctypes.POINTER(_PlanParams),
+                                          pi32, pi32, pi32, ctypes.POINTER(_PlanInfo)]
+    lib.mla_choose_partitions.restype = ctypes.c_int
+    lib.mla_partition_range.argtypes = [i32, i32, i32, i32, i32, i32, pi32, pi32]
+    lib.mla_partition_range.restype = ctypes.c_int
+    lib.mla_decode_partition.argtypes = [vp, vp, vp, vp, i32, vp, i32, vp, i32, i32,
+                                         ctypes.c_float, i32, vp, vp, vp, i32, i32, i32,
+                                         vp, vp, vp, vp, vp, vp]
+    lib.mla_decode_partition.restype = ctypes.c_int
+    lib.mla_decode_reduce.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
+    lib.mla_decode_reduce.restype = ctypes.c_int
+    lib.mla_status_string.argtypes = [ctypes.c_int]
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_last_error.argtypes = []
+    lib.mla_last_error.restype = ctypes.c_char_p
+    lib.mla_get_counters.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
+    lib.mla_get_counters.restype = None
+    lib.mla_reset_counters.argtypes = []
+    lib.mla_reset_counters.restype = None
+    del i64
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = load_library().mla_last_error().decode(errors="replace")
+        raise MlaError(status, msg)
+
+
+@dataclasses.dataclass
+class PlanParams:
+    """Mirror of mla_plan_params (defaults from mla_default_plan_params)."""
+    min_split_ctx: int = 32768
+    tokens_per_partition: int = 16384
+    min_partitions: int = 2
+    max_partitions: int = 8
+    num_cus: int = 0
+    heads_per_wg: int = 0
+    min_tile_blocks: int = 4
+    wgs_per_cu: int = 1
+    force_partitions: int = 0
+    force_splits: int = 0
+    workspace_limit_bytes: int = 0
+
+    def _c(self) -> _PlanParams:
+        return _PlanParams(**dataclasses.asdict(self))
+
+
+def mla_default_plan_params() -> PlanParams:
+    lib = load_library()
+    p = _PlanParams()
+    lib.mla_default_plan_params(ctypes.byref(p))
+    return PlanParams(**{f: getattr(p, f) for f, _ in _PlanParams._fields_})
+
+
+def _i32_array(values):
+    values = [int(v) for v in values]
+    return (ctypes.c_int32 * max(1, len(values)))(*values)
+
+
+def mla_choose_partitions(batch: int, num_heads: int, q_len: int, context_lens,
+                          params: PlanParams | None = None, block_size: int = BLOCK_SIZE) -> dict:
+    """Host chooser: returns P, S, row_indptr (lists) and the plan info."""
+    lib = load_library()
+    ctx = _i32_array(context_lens)
+    P = (ctypes.c_int32 * max(1, batch))()
+    S = (ctypes.c_int32 * max(1, batch))()
+    ind = (ctypes.c_int32 * (batch + 1))()
+    info = _PlanInfo()
+    prm = params._c() if params is not None else None
+    _check(lib.mla_choose_partitions(batch, num_heads, q_len, ctx, block_size,
+                                     ctypes.byref(prm) if prm is not None else None,
+                                     P, S, ind, ctypes.byref(info)))
+    out = {f: getattr(info, f) for f, _ in _PlanInfo._fields_}
+    out.update(P=list(P)[:batch], S=list(S)[:batch], row_indptr=list(ind))
+    return out
+
+
+def mla_partition_range(ctx: int, P: int, S: int, p: int, s: int,
+                        block_size: int = BLOCK_SIZE):
+    lib = load_library()
+    lo, hi = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib.mla_partition_range(ctx, block_size, P, S, p, s, ctypes.byref(lo), ctypes.byref(hi)))
+    return lo.value, hi.value
+
+
+def mla_status_string(status: int) -> str:
+    return load_library().mla_status_string(status).decode()
+
+
+def mla_last_error() -> str:
+    return load_library().mla_last_error().decode(errors="replace")
+
+
+def mla_get_counters():
+    arr = (ctypes.c_uint64 * 4)()
+    load_library().mla_get_counters(arr)
+    return list(arr)
+
+
+def mla_reset_counters():
+    load_library().mla_reset_counters()
+
+
+# ---------------------------------------------------------------------------
+# Device-side calls (torch tensors in, pointers out).
+# ---------------------------------------------------------------------------
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float16:
+        return MLA_F16
+    if t.dtype == torch.bfloat16:
+        return MLA_BF16
+    raise MlaError(-6, f"16-bit tensors must be float16 or bfloat16, got {t.dtype}")
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise MlaError(-1, "device tensors are required (torch CUDA/HIP tensors)")
+
+
+def mla_decode_partition(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens,
+                         scale: float, partitions, splits, row_indptr, total_rows: int,
+                         max_rows_per_req: int, heads_per_wg: int, partial_out, partial_lse2,
+                         out, lse2_out=None, debug_ranges=None, stream=None):
+    """Launch the partition kernel (see include/mla_decode.h)."""
+    lib = load_library()
+    _need_cuda(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens)
+    B, H = int(q_absorbed.shape[0]), int(q_absorbed.shape[1])
+    _check(lib.mla_decode_partition(
+        _ptr(q_absorbed), _ptr(q_pe), _ptr(ckv_cache), _ptr(kpe_cache), int(ckv_cache.shape[0]),
+        _ptr(block_table), int(block_table.shape[1]), _ptr(context_lens), B, H,
+        float(scale), _dtype_code(q_absorbed), _ptr(partitions), _ptr(splits), _ptr(row_indptr),
+        int(total_rows), int(max_rows_per_req), int(heads_per_wg), _ptr(partial_out),
+        _ptr(partial_lse2), _ptr(out), _ptr(lse2_out), _ptr(debug_ranges), _stream(stream)))
+
+
+def mla_decode_reduce(partial_out, partial_lse2, row_indptr, batch: int, num_heads: int,
+                      total_rows: int, out, lse2_out=None, stream=None):
+    """Launch the LSE-weighted reduce (see include/mla_decode.h)."""
+    lib = load_library()
+    _need_cuda(partial_out, partial_lse2, row_indptr, out)
+    _check(lib.mla_decode_reduce(_ptr(partial_out), _ptr(partial_lse2), _ptr(row_indptr),
+                                 int(batch), int(num_heads), int(total_rows), _dtype_code(out),
+                                 _ptr(out), _ptr(lse2_out), _stream(stream)))
+
+
+class DecodePlan:
+    """A chooser result with its arrays and workspace on the device."""
+
+    def __init__(self, context_lens, num_heads: int, params: PlanParams | None = None,
+                 device="cuda", q_len: int = 1):
+        import torch
+        ctx = [int(c) for c in context_lens]
+        self.batch = len(ctx)
+        self.heads = num_heads
+        self.info = mla_choose_partitions(self.batch, num_heads, q_len, ctx, params)
+        i32 = torch.int32
+        self.partitions = torch.tensor(self.info["P"], dtype=i32, device=device)
+        self.splits = torch.tensor(self.info["S"], dtype=i32, device=device)
+        self.row_indptr = torch.tensor(self.info["row_indptr"], dtype=i32, device=device)
+        rows = max(1, self.info["total_rows"])
+        if self.info["needs_reduce"]:
+            self.partial_out = torch.empty((rows, num_heads, KV_LORA_RANK), dtype=torch.float32,
+                                           device=device)
+            self.partial_lse2 = torch.empty((rows, num_heads), dtype=torch.float32, device=device)
+        else:
+            self.partial_out = self.partial_lse2 = None
+
+    @property
+    def total_rows(self) -> int:
+        return self.info["total_rows"]
+
+
+def decode(plan: DecodePlan, q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens,
+           scale: float, out, lse2_out=None, debug_ranges=None, stream=None):
+    """Partition launch, then the reduce launch when the plan needs one."""
+    mla_decode_partition(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens, scale,
+                         plan.partitions, plan.splits, plan.row_indptr, plan.total_rows,
+                         plan.info["max_rows_per_req"], plan.info["heads_per_wg"],
+                         plan.partial_out, plan.partial_lse2, out,
+                         lse2_out if not plan.info["needs_reduce"] else None,
+                         debug_ranges, stream)
+    if plan.info["needs_reduce"]:
+        mla_decode_reduce(plan.partial_out, plan.partial_lse2, plan.row_indptr, plan.batch,
+                          plan.heads, plan.total_rows, out, lse2_out, stream)

@@ -1,0 +1,90 @@
+// Device-side helpers shared by the gfx950 kernels of this library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+namespace dev {
+
+#define MLA_LDS __attribute__((address_space(3)))
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 16-bit element traits: MFMA operand vectors and round-to-nearest-even
+// conversion from fp32 for fp16 (MLA_F16) and bfloat16 (MLA_BF16).
+template <int DT> struct Elem;
+template <> struct Elem<0> {
+  typedef f16x8 vec8;
+  typedef f16x4 vec4;
+  typedef _Float16 scalar;
+  static __device__ __forceinline__ f32x4 mfma(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ vec4 tr_read(const MLA_LDS void* p) {
+    typedef __fp16 fp16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+    return __builtin_bit_cast(vec4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((MLA_LDS fp16x4*)p));
+  }
+};
+template <> struct Elem<1> {
+  typedef bf16x8 vec8;
+  typedef bf16x4 vec4;
+  typedef __bf16 scalar;
+  static __device__ __forceinline__ f32x4 mfma(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ vec4 tr_read(const MLA_LDS void* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS vec4*)p);
+  }
+};
+
+// Wait until at most N vector-memory operations of this wave are
+// outstanding (s_waitcnt vmcnt(N); expcnt and lgkmcnt left alone).
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One 16-byte-per-lane copy from global memory straight into LDS: lane i's
+// 16 bytes land at lds_base + 16 * i (global_load_lds_dwordx4). Issued from
+// inline assembly so that the compiler does not put a full vmcnt(0) wait in
+// front of every later LDS read: the kernel waits for each stage itself.
+// M0 takes the wave-uniform LDS base; one wait state separates the M0 write
+// from the load that reads it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is set and consumed inside the statement
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Read-only int32 metadata (block table, plan arrays) through the constant
+// address space: uniform loads then become scalar (s_load, counted by
+// lgkmcnt), so they never wait behind the in-flight LDS DMA on vmcnt.
+#define MLA_CONST __attribute__((address_space(4)))
+__device__ __forceinline__ int32_t load_const(const int32_t* p, int64_t i) {
+  return ((const MLA_CONST int32_t*)p)[i];
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const MLA_LDS void* p) {
+  return (uint32_t)(uintptr_t)p;
+}
+
+__device__ __forceinline__ float shfl_xor(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+}  // namespace dev
+}  // namespace mla

@@ -1,0 +1,226 @@
+"""Decode-latency benchmark of split-KV absorbed-MLA decode on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one decode batch: the host
+partition chooser, the partition kernel and (when the plan splits) the
+LSE-weighted reduce. Inputs are synthetic and resident in HBM before timing
+starts. To keep the 256 MB Infinity Cache from serving repeated reads, each
+step reads a different copy of the KV pool (enough copies that the steps'
+working set is several times the cache). The K timed steps are captured into
+one HIP graph and replayed once between two HIP events, so host launch cost
+does not pad the figure.
+
+Prints one JSON line on stdout (details on stderr). ``value`` is the decode
+latency in microseconds per step (lower is better). ``roofline`` is for the
+partition kernel: algorithmic bytes of one launch over its mean duration,
+taken with HIP events around back-to-back launches on the launch stream.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+KV_BYTES_PER_TOKEN = (512 + 64) * 2
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(case):
+    """KV rows read + q read + out written + table and context lengths."""
+    tokens = int(case.context_lens.astype(np.int64).sum())
+    nblk = int(sum((int(n) + 31) // 32 for n in case.context_lens))
+    kv = tokens * KV_BYTES_PER_TOKEN
+    q = case.batch * case.heads * (512 + 64) * 2
+    out = case.batch * case.heads * 512 * 2
+    meta = nblk * 4 + case.batch * 4
+    return dict(kv=kv, q=q, out=out, meta=meta, total=kv + q + out + meta,
+                partition=kv + q + meta, tokens=tokens)
+
+
+def cpu_baseline(case, budget_s: float):
+    """Time the f64 oracle on the same workload; repeat to fill ~budget_s."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    oracle.latent_f64(case)
+    one = time.perf_counter() - t0
+    reps = max(1, min(50, int(budget_s / max(one, 1e-3))))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.latent_f64(case)
+    per = (time.perf_counter() - t0) / reps
+    return dict(value=round(per * 1e6, 1), unit="us", cores=cores, kind="oracle",
+                sample=f"whole workload (all requests and heads), f64 numpy, {reps} timed "
+                       f"repetitions after one warm-up, {per * reps:.1f} s of CPU time")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="v2lite_32k")
+    ap.add_argument("--single-pass", action="store_true", help="force P = S = 1")
+    ap.add_argument("--cold-bytes", type=float, default=1.5e9,
+                    help="bytes of distinct KV copies cycled through (MALL is 256 MB)")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=100)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "this build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    rank = int(os.environ.get("RANK", "0"))
+
+    import torch
+    import absorbed_mla_paged_amd as mla
+    import mla_synth
+
+    log(f"[bench] workload={args.workload} steps={args.steps} warmup={args.warmup}")
+    case = mla_synth.make_workload(args.workload)
+    alg = algorithmic_bytes(case)
+    td = torch.float16 if case.dtype == "f16" else torch.bfloat16
+    dev = torch.device("cuda", 0)
+
+    def t16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(td).to(dev)
+
+    ckv = t16(case.ckv_pool)
+    kpe = t16(case.kpe_pool)
+    pool_bytes = ckv.numel() * 2 + kpe.numel() * 2
+    ncopy = max(1, min(64, math.ceil(args.cold_bytes / max(1, alg["kv"]))))
+    copies = [(ckv, kpe)] + [(ckv.clone(), kpe.clone()) for _ in range(ncopy - 1)]
+    qa, qp = t16(case.q_absorbed), t16(case.q_pe)
+    table = torch.from_numpy(case.block_table).to(dev)
+    ctx = torch.from_numpy(case.context_lens).to(dev)
+    prm = mla.PlanParams(force_partitions=1, force_splits=1) if args.single_pass else None
+    plan = mla.DecodePlan(case.context_lens, case.heads, prm, device=dev)
+    info = plan.info
+    out = torch.empty((case.batch, case.heads, 512), dtype=td, device=dev)
+    lse2 = torch.empty((case.batch, case.heads), dtype=torch.float32, device=dev)
+    log(f"[bench] plan P={info['P']} S={info['S']} rows={info['total_rows']} "
+        f"tile={info['tile_blocks']} reduce={info['needs_reduce']} copies={ncopy} "
+        f"pool={pool_bytes / 1e6:.1f} MB")
+
+    def step(j):
+        # Host chooser (same contexts every step, so the device plan arrays
+        # already hold its answer), then the device work.
+        mla.mla_choose_partitions(case.batch, case.heads, 1, case.context_lens, prm)
+        c, k = copies[j % ncopy]
+        mla.decode(plan, qa, qp, c, k, table, ctx, case.scale, out, lse2)
+
+    stream = torch.cuda.Stream(device=dev)
+    torch.cuda.synchronize()
+    # Eager reference result, then graph capture of the timed steps.
+    with torch.cuda.stream(stream):
+        step(0)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    with torch.cuda.stream(stream):
+        for j in range(args.warmup):
+            step(j)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for j in range(args.steps):
+            step(j)
+    torch.cuda.synchronize()
+    graph.replay()            # untimed replay (also checks the graph result)
+    torch.cuda.synchronize()
+    if not torch.equal(out, eager):
+        log("[bench] graph replay differs from the eager result")
+        sys.exit(3)
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    if not torch.equal(out, eager):
+        log("[bench] timed replay differs from the eager result")
+        sys.exit(3)
+    ms_per_step = gpu_ms / args.steps
+    log(f"[bench] {args.steps} steps: {gpu_ms:.3f} ms GPU ({wall * 1e3:.3f} ms wall) "
+        f"-> {ms_per_step * 1e3:.2f} us/step")
+
+    # Partition kernel alone: back-to-back launches (rotating copies) in a
+    # graph, HIP events on the launch stream around them.
+    reps = args.kernel_reps
+    kgraph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(kgraph, stream=stream):
+        for j in range(reps):
+            c, k = copies[j % ncopy]
+            mla.mla_decode_partition(qa, qp, c, k, table, ctx, case.scale, plan.partitions,
+                                     plan.splits, plan.row_indptr, plan.total_rows,
+                                     info["max_rows_per_req"], info["heads_per_wg"],
+                                     plan.partial_out, plan.partial_lse2, out, lse2)
+    kgraph.replay()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        kgraph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    part_us = e0.elapsed_time(e1) * 1e3 / reps
+    achieved = alg["partition"] / (part_us * 1e-6) / 1e9
+    split_bytes = info["total_rows"] * case.heads * 513 * 4 if info["needs_reduce"] else 0
+    pair_gbs = alg["total"] / (ms_per_step * 1e-3) / 1e9
+    log(f"[bench] partition kernel {part_us:.2f} us -> {achieved:.0f} GB/s "
+        f"({100 * achieved / HBM_PEAK_GBS:.1f}% of 8 TB/s); pair {pair_gbs:.0f} GB/s; "
+        f"split overhead {split_bytes / 1e6:.2f} MB written")
+
+    cpu = None
+    if rank == 0 and not args.no_cpu:
+        cpu = cpu_baseline(case, args.cpu_budget)
+        log(f"[bench] cpu oracle {cpu}")
+
+    line = {
+        "metric": "decode latency (µs) + achieved HBM GB/s vs peak, absorbed-MLA 32K–131K ctx",
+        "value": round(ms_per_step * 1e3, 3),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f16": "f16", "bf16": "bf16"}[case.dtype],
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": case.batch, "heads": case.heads,
+                   "context_lens": [int(n) for n in case.context_lens],
+                   "block_size": 32, "kv_lora_rank": 512, "rope_dim": 64,
+                   "plan": {"P": info["P"], "S": info["S"], "rows": info["total_rows"]},
+                   "single_pass": bool(args.single_pass), "kv_copies": ncopy},
+        "achieved_gbs_pair": round(pair_gbs, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "partition_kernel",
+                     "kernel_us": round(part_us, 3),
+                     "algorithmic_bytes": alg["partition"]},
+        "cpu_baseline": cpu,
+        "host": platform.node(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
