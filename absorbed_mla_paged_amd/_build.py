@@ -28,6 +28,7 @@ def command(out: str = LIB, extra=()) -> list[str]:
     return [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-Wall", "-Wno-unused-function",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-kernarg-preload-count=16",
             "-I", os.path.join(HERE, "..", "include"),
             *extra, "-o", out, *[os.path.join(CSRC, s) for s in SOURCES]]
 

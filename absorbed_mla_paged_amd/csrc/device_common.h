@@ -20,12 +20,19 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // 16-bit element traits: MFMA operand vectors and round-to-nearest-even
 // conversion from fp32 for fp16 (MLA_F16) and bfloat16 (MLA_BF16).
 template <int DT> struct Elem;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
 template <> struct Elem<0> {
   typedef f16x8 vec8;
   typedef f16x4 vec4;
   typedef _Float16 scalar;
+  // D = A(16x32) B(32x16) + C
   static __device__ __forceinline__ f32x4 mfma(vec8 a, vec8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  // D = A(16x16) B(16x16) + C
+  static __device__ __forceinline__ f32x4 mfma16(vec4 a, vec4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ vec4 tr_read(const MLA_LDS void* p) {
     typedef __fp16 fp16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
@@ -39,6 +46,10 @@ template <> struct Elem<1> {
   static __device__ __forceinline__ f32x4 mfma(vec8 a, vec8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
+  static __device__ __forceinline__ f32x4 mfma16(vec4 a, vec4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                      __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+  }
   static __device__ __forceinline__ vec4 tr_read(const MLA_LDS void* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS vec4*)p);
   }
@@ -49,6 +60,11 @@ template <> struct Elem<1> {
 template <int N> __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait until every LDS / scalar-memory operation of this wave has completed.
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
 }
 
 // One 16-byte-per-lane copy from global memory straight into LDS: lane i's

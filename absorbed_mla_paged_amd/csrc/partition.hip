@@ -9,29 +9,32 @@
 // normalised fp32 partial and its base-2 log-sum-exp, or rounded straight
 // into `out` when the request is a single row.
 //
-// Mapping onto one CU (256 threads = 4 wave64):
-//  * Paged gather: each 32-token cache block (32 KB of ckv + 4 KB of kpe,
-//    contiguous per physical block) is copied by global_load_lds_dwordx4
-//    (16 B per lane, whole 128 B lines per instruction) into one of 4 LDS
-//    stages of a ring, so up to 4 blocks per CU are in flight. Within a
-//    row, the 16-byte chunk c sits at chunk position c ^ swz(row), which
-//    keeps both the row-wise reads of the score product and the transposed
+// Mapping onto one CU: 512 threads = 8 wave64, two per SIMD.
+//  * Stages: the row is cut into stages of two 32-token cache blocks
+//    (64 KB of ckv + 8 KB of kpe), held in two alternating LDS slots.
+//  * Copy waves (4..7) move stages in with global_load_lds_dwordx4 (16 B per
+//    lane, one 1 KB row per instruction, so whole 128 B lines). Once the
+//    memory queue of the CU is full, issuing a copy blocks the issuing wave;
+//    keeping copies on their own waves means that block never delays the
+//    arithmetic. Copy waves 4,5 serve slot 0, waves 6,7 slot 1; each waits
+//    for its own copies and then bumps the slot's "ready" counter in LDS.
+//  * Compute waves (0..3) wait on those counters, never on memory, and bump
+//    the slot's "free" counter when done with it.
+//  * Within an LDS row the 16-byte chunk c sits at position c ^ swz(row),
+//    which keeps the row-wise reads of the score product and the transposed
 //    reads of the value product free of bank conflicts.
 //  * Scores: S^T[token, head] = K[token, :] . Q^T[:, head] on
-//    v_mfma_f32_16x16x32 (K = 576 = 18 steps of 32), tokens as the M side
-//    and the 16 heads as the N side. Q (16 x 576) stays in registers.
-//  * Online softmax in the base-2 domain: each lane owns one head and 8
-//    tokens of a block; the block maximum needs two cross-lane steps. The
-//    running reference maximum is only moved when a block beats it by more
-//    than 2^8, so rescaling the fp32 accumulators is rare; the final O/l is
-//    unchanged by that choice.
-//  * Values: O^T[dim, head] += V^T[dim, token] . P^T[token, head], with the
-//    probabilities P^T taken straight from the score accumulators (the MFMA
-//    output layout of S^T is exactly the B-operand layout of this product
-//    once the 32 tokens are ordered to match) and V^T read from the same
-//    LDS tile with ds_read_b64_tr_b16. The 4 waves split the 512 output
-//    dims (128 each), so every wave computes the scores of all 32 tokens --
-//    cheap at 16 heads, where the kernel is bound by HBM many times over.
+//    v_mfma_f32_16x16x32 (K = 576 = 18 steps); compute wave w scores the
+//    stage's 16-token tile w. Q (16 x 576) sits in their registers.
+//  * Online softmax in the base-2 domain: the tile maxima of each head meet
+//    in LDS; the running maximum only moves when a stage beats it by more
+//    than 2^8, so rescaling is rare. Each compute wave writes its tile's
+//    probabilities to LDS in the B-operand layout of the value product. The
+//    compute waves meet through LDS counters as well (never s_barrier, which
+//    would also wait for the copy waves).
+//  * Values: O^T[dim, head] += V^T[dim, token] . P^T[token, head] on
+//    v_mfma_f32_16x16x32; V^T is read from the same LDS tile with
+//    ds_read_b64_tr_b16. Compute wave w owns dims [128 w, 128 w + 128).
 #include "device_common.h"
 #include "internal.h"
 
@@ -42,93 +45,95 @@ namespace {
 
 using namespace dev;
 
-constexpr int BS = MLA_BLOCK_SIZE;            // tokens per cache block
-constexpr int LAT = MLA_KV_LORA_RANK;         // 512
-constexpr int ROPE = MLA_ROPE_DIM;            // 64
-constexpr int CKV_ROW = LAT * 2;              // bytes per ckv row
-constexpr int KPE_ROW = ROPE * 2;             // bytes per kpe row
-constexpr int CKV_TILE = BS * CKV_ROW;        // 32 KB
-constexpr int KPE_TILE = BS * KPE_ROW;        // 4 KB
-constexpr int STAGE = CKV_TILE + KPE_TILE;    // 36 KB per cache block
-constexpr int NSTAGE = 4;
-constexpr int WAVES = 4;
-constexpr int THREADS = 64 * WAVES;
-constexpr int HG = 16;                        // heads per workgroup
-constexpr int KSTEPS = (LAT + ROPE) / 32;     // 18 MFMA K-steps per score
-constexpr int DT_PER_WAVE = LAT / 16 / WAVES; // 8 output dim tiles per wave
-constexpr int LOADS_PER_BLOCK = STAGE / 1024 / WAVES;  // 9 DMA ops per wave
-constexpr float RESCALE_LOG2 = 8.0f;          // lazy-rescale threshold
-static_assert(LOADS_PER_BLOCK * WAVES * 1024 == STAGE, "stage split");
-static_assert(NSTAGE * STAGE <= 160 * 1024, "LDS budget");
-// Q (16 heads x 1152 B) is staged through the last ring stage at start.
-static_assert(HG * (CKV_ROW + KPE_ROW) <= STAGE, "Q staging fits a stage");
+constexpr int BS = MLA_BLOCK_SIZE;              // tokens per cache block
+constexpr int LAT = MLA_KV_LORA_RANK;           // 512
+constexpr int ROPE = MLA_ROPE_DIM;              // 64
+constexpr int CKV_ROW = LAT * 2;                // bytes per ckv row
+constexpr int KPE_ROW = ROPE * 2;               // bytes per kpe row
+constexpr int ST_TOK = 2 * BS;                  // tokens per stage
+constexpr int ST_KPE = ST_TOK * CKV_ROW;        // kpe rows after the ckv rows
+constexpr int STAGE = ST_TOK * (CKV_ROW + KPE_ROW);   // 72 KB
+constexpr int CWAVES = 4;                       // compute waves
+constexpr int THREADS = 64 * 2 * CWAVES;        // plus as many copy waves
+constexpr int HG = 16;                          // heads per workgroup
+constexpr int KSTEPS = (LAT + ROPE) / 32;       // 18 score K-steps
+constexpr int DT_PER_WAVE = LAT / 16 / CWAVES;  // 8 output dim tiles per wave
+constexpr int OPS_PER_COPY = STAGE / 1024 / 2;  // 36 copies per copy wave
+constexpr float RESCALE_LOG2 = 8.0f;            // lazy-rescale threshold
+// After the two slots: counters ready[2], free[2], issued, maxima, probs;
+// the tile maxima [4][16]; the P fragments [2 K-steps][64 lanes][16 B].
+constexpr int XCNT = 2 * STAGE;
+constexpr int XMAX = XCNT + 64;
+constexpr int XP = XMAX + CWAVES * HG * 4;
+constexpr int LDS_BYTES = XP + 2 * 64 * 16;
+static_assert(OPS_PER_COPY * 2 * 1024 == STAGE, "stage split");
+static_assert(OPS_PER_COPY < 64, "vmcnt range");
+static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
+// Arguments the start of every workgroup waits on. They are passed as the
+// first kernel arguments (16 dwords), which gfx950 preloads into SGPRs at
+// wave launch, so finding the row costs no argument fetch.
+struct RowArgs {
+  int32_t groups;        // heads / HG
+  int32_t rows_per_req;  // grid rows per request (max_rows_per_req)
+  int32_t slots;         // batch * rows_per_req
+  int32_t direct;        // 1: one row per request, write `out`
+  int32_t total_rows;
+  int32_t max_blocks;
+  const int32_t* context_lens;
+  const int32_t* row_indptr;
+  const int32_t* partitions;
+  const int32_t* splits;
+  const int32_t* block_table;
+};
+
+// The rest, fetched from the argument segment while the row is looked up.
 struct PartitionArgs {
   const uint16_t* q_absorbed;
   const uint16_t* q_pe;
   const uint16_t* ckv;
   const uint16_t* kpe;
-  const int32_t* block_table;
-  const int32_t* context_lens;
-  const int32_t* partitions;
-  const int32_t* splits;
-  const int32_t* row_indptr;
   float* partial_out;
   float* partial_lse2;
   void* out;
   float* lse2_out;
   int32_t* debug_ranges;
   int32_t num_blocks;
-  int32_t max_blocks;
-  int32_t batch;
   int32_t heads;
-  int32_t groups;        // heads / HG
-  int32_t rows_per_req;  // grid rows per request (max_rows_per_req)
-  int32_t slots;         // batch * rows_per_req
-  int32_t total_rows;
-  int32_t direct;        // 1: one row per request, write `out`
   float scale_log2;      // scale * log2(e)
 };
 
-// XOR swizzles of the 16-byte chunk index inside an LDS row (see header).
+// XOR swizzles of the 16-byte chunk index inside an LDS row.
 __device__ __forceinline__ int swz_ckv(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 __device__ __forceinline__ int swz_kpe(int r) { return (r >> 1) & 7; }
 
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
-// Issue the DMA of one 32-token cache block into `stage` (9 ops per wave).
-__device__ __forceinline__ void issue_block(const PartitionArgs& a, int64_t phys,
-                                            uint32_t stage, int wave, int lane) {
-  const char* ckv = reinterpret_cast<const char*>(a.ckv) + phys * CKV_TILE;
-  const char* kpe = reinterpret_cast<const char*>(a.kpe) + phys * KPE_TILE;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = wave * 8 + j;
-    const int chunk = (lane & ~15) | ((lane & 15) ^ swz_ckv(r));
-    dma16(ckv + r * CKV_ROW + chunk * 16, stage + r * CKV_ROW);
-  }
-  {
-    const int r = wave * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ swz_kpe(r);
-    dma16(kpe + r * KPE_ROW + chunk * 16, stage + CKV_TILE + wave * 1024);
-  }
+// Spin until the LDS counter reaches `target` (the waves of a workgroup are
+// all resident, and every counter a wave waits on is bumped by waves that do
+// not wait on this one first, so the wait ends).
+__device__ __forceinline__ void wait_counter(const MLA_LDS uint32_t* c, uint32_t target) {
+  while (*(const volatile MLA_LDS uint32_t*)c < target) __builtin_amdgcn_s_sleep(1);
+  asm volatile("" ::: "memory");
 }
 
-// Wait until this wave's DMA ops older than the newest `ahead` blocks are
-// complete (ahead = blocks issued after the one we need).
-__device__ __forceinline__ void wait_blocks_ahead(int ahead) {
-  if (ahead >= 3) wait_vmcnt<3 * LOADS_PER_BLOCK>();
-  else if (ahead == 2) wait_vmcnt<2 * LOADS_PER_BLOCK>();
-  else if (ahead == 1) wait_vmcnt<LOADS_PER_BLOCK>();
-  else wait_vmcnt<0>();
+__device__ __forceinline__ void bump_counter(MLA_LDS uint32_t* c, int lane) {
+  wait_lgkmcnt0();   // this wave's LDS reads / writes before the bump are done
+  if (lane == 0) __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 template <int DT>
-__global__ __launch_bounds__(THREADS) void partition_kernel(PartitionArgs a) {
+__global__ __launch_bounds__(THREADS) void partition_kernel(
+    int32_t groups, int32_t rows_per_req, int32_t slots, int32_t direct, int32_t total_rows,
+    int32_t max_blocks, const int32_t* __restrict__ context_lens,
+    const int32_t* __restrict__ row_indptr, const int32_t* __restrict__ partitions,
+    const int32_t* __restrict__ splits, const int32_t* __restrict__ block_table,
+    PartitionArgs a) {
   typedef Elem<DT> E;
   typedef typename E::vec8 vec8;
   typedef typename E::vec4 vec4;
-  __shared__ __attribute__((aligned(1024))) char smem_raw[NSTAGE * STAGE];
+  typedef typename E::scalar scalar;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[LDS_BYTES];
   MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
 
   const int tid = threadIdx.x;
@@ -136,6 +141,7 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(PartitionArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 15;   // MFMA row/column inside a 16-wide tile
   const int lg = lane >> 4;   // MFMA k-group (0..3)
+  const bool copier = wave >= CWAVES;
 
   // ---- which (request, local row, head group) this workgroup owns -------
   // Workgroups are dealt to the 8 XCDs round-robin by linear id. Row slot
@@ -143,23 +149,44 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(PartitionArgs a) {
   // keeps the G head groups of one row on one XCD, so they share its L2.
   const int L = blockIdx.x;
   const int sl = L >> 3;
-  const int hg = sl % a.groups;
-  const int u = (sl / a.groups) * 8 + (L & 7);
-  if (u >= a.slots) return;
-  const int b = u / a.rows_per_req;
-  const int x = u % a.rows_per_req;
+  const int hg = sl % groups;
+  const int u = (sl / groups) * 8 + (L & 7);
+  if (u >= slots) return;
+  const int b = u / rows_per_req;
+  const int x = u % rows_per_req;
 
-  int n = load_const(a.context_lens, b);
-  n = max(0, min(n, a.max_blocks * BS));
+  const int head0 = hg * HG;
+  const int64_t qrow0 = (int64_t)b * a.heads + head0;   // first (b, head) row
+  const int my_head = head0 + ln;
+
+  // Q (compute waves): issued first, its address needs no metadata. B
+  // operand of the score product: lane (ln, lg) holds head head0 + ln, dims
+  // 32 k + 8 lg .. + 8. Compute waves issue no copies, so the compiler's
+  // own wait for Q is exact.
+  vec8 q[KSTEPS];
+  if (!copier) {
+    const vec8* qa = reinterpret_cast<const vec8*>(a.q_absorbed + (qrow0 + ln) * LAT);
+    const vec8* qp = reinterpret_cast<const vec8*>(a.q_pe + (qrow0 + ln) * ROPE);
+#pragma unroll
+    for (int k = 0; k < KSTEPS; ++k)
+      q[k] = (k < LAT / 32) ? qa[4 * k + lg] : qp[4 * (k - LAT / 32) + lg];
+  }
+
+  // All row metadata in one round trip.
+  int n = load_const(context_lens, b);
   int P = 1, S = 1, row = b, nrows = 1;
-  if (!a.direct) {
-    const int r0 = load_const(a.row_indptr, b);
-    nrows = load_const(a.row_indptr, b + 1) - r0;
-    P = max(1, min(load_const(a.partitions, b), 1 << 25));
-    S = max(1, min(load_const(a.splits, b), 1 << 25));
+  if (!direct) {
+    const int r0 = load_const(row_indptr, b);
+    const int r1 = load_const(row_indptr, b + 1);
+    const int pv = load_const(partitions, b);
+    const int sv = load_const(splits, b);
+    nrows = r1 - r0;
+    P = max(1, min(pv, 1 << 25));
+    S = max(1, min(sv, 1 << 25));
     row = r0 + x;
   }
-  if (x >= nrows || row < 0 || row >= a.total_rows) return;
+  n = max(0, min(n, max_blocks * BS));
+  if (x >= nrows || row < 0 || row >= total_rows) return;
   const int p = x / S;
   const int s = x % S;
   // Index math of mla_partition_range (must agree bit for bit).
@@ -173,28 +200,17 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(PartitionArgs a) {
   const int blk_hi = (p < P) ? pb0 + min((s + 1) * bps, m) : nblk;
   const int tok_lo = min(blk_lo * BS, n);
   const int tok_hi = min(blk_hi * BS, n);
-  const int nb = blk_hi - blk_lo;
+  const int nblocks = cdiv(tok_hi - tok_lo, BS);   // non-empty blocks
+  const int nst = cdiv(nblocks, 2);                 // stages
 
-  const int head0 = hg * HG;
-  const int64_t qrow0 = (int64_t)b * a.heads + head0;   // first (b, head) row
-  const int my_head = head0 + ln;
-
-  if (a.debug_ranges && hg == 0 && tid == 0) {
-    // Stored before any DMA is issued only on the empty path; otherwise in
-    // the epilogue, so no store is outstanding while stages are awaited.
-    if (nb <= 0 || tok_hi <= tok_lo) {
-      a.debug_ranges[2 * row] = tok_lo;
-      a.debug_ranges[2 * row + 1] = tok_hi;
-    }
-  }
-  if (nb <= 0 || tok_hi <= tok_lo) {
+  if (nst <= 0) {
     // No visible token: zero output, lse2 = -inf.
+    if (copier) return;
 #pragma unroll
     for (int dt = 0; dt < DT_PER_WAVE; ++dt) {
       const int d0 = (wave * DT_PER_WAVE + dt) * 16 + lg * 4;
-      const int64_t off = ((int64_t)b * a.heads + my_head) * LAT + d0;
-      if (a.direct) {
-        uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + off;
+      if (direct) {
+        uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)b * a.heads + my_head) * LAT + d0;
         *reinterpret_cast<u32x2*>(o) = u32x2{0u, 0u};
       } else {
         float* o = a.partial_out + ((int64_t)row * a.heads + my_head) * LAT + d0;
@@ -202,141 +218,152 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(PartitionArgs a) {
       }
     }
     if (wave == 0 && lg == 0) {
-      if (a.direct) {
+      if (direct) {
         if (a.lse2_out) a.lse2_out[(int64_t)b * a.heads + my_head] = -INFINITY;
       } else {
         a.partial_lse2[(int64_t)row * a.heads + my_head] = -INFINITY;
       }
     }
+    if (a.debug_ranges && hg == 0 && tid == 0) {
+      a.debug_ranges[2 * row] = tok_lo;
+      a.debug_ranges[2 * row + 1] = tok_hi;
+    }
     return;
   }
 
-  const int64_t tbl0 = (int64_t)b * a.max_blocks;
-  const int last_blk = a.num_blocks - 1;
-  auto phys_of = [&](int blk) -> int64_t {
-    int v = __builtin_amdgcn_readfirstlane(load_const(a.block_table, tbl0 + blk));
-    return (int64_t)max(0, min(v, last_blk));
-  };
-  const uint32_t lds0 = lds_addr(smem);
-
-  // ---- prologue: Q into the last stage, first blocks into the others ----
-  {
-    const uint32_t qst = lds0 + (NSTAGE - 1) * STAGE;
-    const char* qa = reinterpret_cast<const char*>(a.q_absorbed) + qrow0 * CKV_ROW;
-#pragma unroll
-    for (int j = 0; j < HG / WAVES; ++j) {
-      const int h = wave * (HG / WAVES) + j;
-      const int chunk = (lane & ~15) | ((lane & 15) ^ swz_ckv(h));
-      dma16(qa + h * CKV_ROW + chunk * 16, qst + h * CKV_ROW);
-    }
-    if (wave < HG * KPE_ROW / 1024) {
-      const char* qp = reinterpret_cast<const char*>(a.q_pe) + qrow0 * KPE_ROW;
-      const int h = wave * 8 + (lane >> 3);
-      const int chunk = (lane & 7) ^ swz_kpe(h);
-      dma16(qp + h * KPE_ROW + chunk * 16, qst + HG * CKV_ROW + wave * 1024);
-    }
-  }
-  int issued = 0;
-  for (; issued < NSTAGE - 1 && issued < nb; ++issued)
-    issue_block(a, phys_of(blk_lo + issued), lds0 + issued * STAGE, wave, lane);
-
-  // Q lands first (oldest ops); wait for it alone.
-  wait_blocks_ahead(issued);
+  MLA_LDS uint32_t* ready = (MLA_LDS uint32_t*)(smem + XCNT);
+  MLA_LDS uint32_t* freed = ready + 2;
+  MLA_LDS uint32_t* issued = ready + 4;
+  MLA_LDS uint32_t* maxed = ready + 5;   // compute waves: maxima written
+  MLA_LDS uint32_t* probs = ready + 6;   // compute waves: P written
+  if (tid < 7) ready[tid] = 0u;
   __syncthreads();
-  vec8 q[KSTEPS];
-  {
-    const MLA_LDS char* qs = smem + (NSTAGE - 1) * STAGE;
+
+  if (copier) {
+    // ---- copy waves: pair `slot` serves stages slot, slot + 2, ... ------
+    const int cw = wave - CWAVES;
+    const int slot = cw >> 1;
+    const int half = cw & 1;            // ops [36 half, 36 half + 36)
+    const int64_t tbl0 = (int64_t)b * max_blocks;
+    const int last_blk = a.num_blocks - 1;
+    const char* ckv_base = reinterpret_cast<const char*>(a.ckv);
+    const char* kpe_base = reinterpret_cast<const char*>(a.kpe);
+    const uint32_t base = lds_addr(smem) + slot * STAGE;
+    for (int k = slot, g = 0; k < nst; k += 2, ++g) {
+      wait_counter(freed + slot, CWAVES * g);
+      // Stages are issued in order, so the memory queue returns them in
+      // order and stage k can be computed while stage k + 1 is arriving.
+      wait_counter(issued, 2 * k);
+      const int nb_here = min(2, nblocks - 2 * k);
+      int64_t phys[2];
 #pragma unroll
-    for (int k = 0; k < KSTEPS; ++k) {
-      const MLA_LDS char* pq;
-      if (k < LAT / 32) {
-        const int c = (4 * k + lg) ^ swz_ckv(ln);
-        pq = qs + ln * CKV_ROW + c * 16;
-      } else {
-        const int c = (4 * (k - LAT / 32) + lg) ^ swz_kpe(ln);
-        pq = qs + HG * CKV_ROW + ln * KPE_ROW + c * 16;
+      for (int j = 0; j < 2; ++j) {
+        // A one-block stage copies its block twice (an L2 hit); its second
+        // half is never read.
+        const int blk = blk_lo + 2 * k + min(j, nb_here - 1);
+        const int v = __builtin_amdgcn_readfirstlane(load_const(block_table, tbl0 + blk));
+        phys[j] = (int64_t)max(0, min(v, last_blk));
       }
-      q[k] = *(const MLA_LDS vec8*)pq;
+      // ops 0..63: ckv rows (block op / 32, row op % 32); 64..71: kpe rows
+      // 8 (op - 64) .. + 8 of the stage.
+#pragma unroll
+      for (int i = 0; i < OPS_PER_COPY; ++i) {
+        const int op = half * OPS_PER_COPY + i;
+        if (op < 64) {
+          const int j = op >> 5, r = op & 31;
+          const int chunk = (lane & ~15) | ((lane & 15) ^ swz_ckv(r));
+          dma16(ckv_base + phys[j] * (BS * CKV_ROW) + r * CKV_ROW + chunk * 16,
+                base + (j * BS + r) * CKV_ROW);
+        } else {
+          const int t8 = op - 64;
+          const int j = t8 >> 2;
+          const int r = (t8 & 3) * 8 + (lane >> 3);
+          const int chunk = (lane & 7) ^ swz_kpe(r);
+          dma16(kpe_base + phys[j] * (BS * KPE_ROW) + r * KPE_ROW + chunk * 16,
+                base + ST_KPE + t8 * 1024);
+        }
+      }
+      if (lane == 0) __hip_atomic_fetch_add(issued, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      wait_vmcnt<0>();
+      const int valid = min(ST_TOK, tok_hi - (tok_lo + k * ST_TOK));
+      if (valid < ST_TOK) {
+        // Rows past the context end may hold anything (NaN included): zero
+        // the latent values of the ones this wave brought in, so that
+        // 0-probability tokens add exactly 0. A one-block stage never reads
+        // rows 32..63.
+        const int zend = min(valid <= BS ? BS : ST_TOK, half ? 64 : 36);
+        const int zbeg = max(valid, half ? 36 : 0);
+        for (int idx = lane; idx < (zend - zbeg) * (CKV_ROW / 16); idx += 64) {
+          const int r = zbeg + idx / (CKV_ROW / 16);
+          const int c = idx % (CKV_ROW / 16);
+          *(MLA_LDS u32x4*)(smem + slot * STAGE + r * CKV_ROW + c * 16) = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+      bump_counter(ready + slot, lane);
     }
-  }
-  __syncthreads();   // everyone holds Q before the last stage is reused
-  if (issued < nb) {
-    issue_block(a, phys_of(blk_lo + issued), lds0 + issued * STAGE, wave, lane);
-    ++issued;
+    return;
   }
 
-  // ---- main loop over the row's cache blocks -----------------------------
+  // ---- compute waves ------------------------------------------------------
   f32x4 o[DT_PER_WAVE];
 #pragma unroll
   for (int dt = 0; dt < DT_PER_WAVE; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY;  // reference maximum (base-2 domain) of my head
-  float l_part = 0.f;       // my 8-token share of the running sum
+  float m_ref = -INFINITY;  // reference maximum of my head, base 2
+  float l_part = 0.f;       // my tile's share of the running sum
   const float c2 = a.scale_log2;
+  MLA_LDS float* max_lds = (MLA_LDS float*)(smem + XMAX);
 
-  for (int i = 0; i < nb; ++i) {
-    const int st = i % NSTAGE;
-    const MLA_LDS char* stg = smem + st * STAGE;
-    // Prefetch the table entry of the block this stage gets next.
-    const bool more = issued < nb;
-    const int64_t next_phys = more ? phys_of(blk_lo + issued) : 0;
+  for (int k = 0; k < nst; ++k) {
+    const int slot = k & 1;
+    const MLA_LDS char* stg = smem + slot * STAGE;
+    const int valid = min(ST_TOK, tok_hi - (tok_lo + k * ST_TOK));
+    wait_counter(ready + slot, 2 * (k / 2 + 1));
 
-    wait_blocks_ahead(issued - i - 1);
-    __syncthreads();
-
-    const int tok0 = (blk_lo + i) * BS;
-    const int valid = min(BS, tok_hi - tok0);  // visible tokens of this block
-    if (valid < BS) {
-      // Rows past the context end may hold anything (NaN included); zero
-      // their latent values so that 0-probability tokens add exactly 0.
-      for (int idx = tid; idx < (BS - valid) * (CKV_ROW / 16); idx += THREADS) {
-        const int r = valid + idx / (CKV_ROW / 16);
-        const int c = idx % (CKV_ROW / 16);
-        *(MLA_LDS u32x4*)(smem + st * STAGE + r * CKV_ROW + c * 16) = u32x4{0u, 0u, 0u, 0u};
-      }
-      __syncthreads();
-    }
-
-    // Scores of the 32 tokens for the 16 heads: two 16-token M-tiles, two
-    // accumulators each (even / odd K-steps) to keep MFMA chains short.
-    f32x4 acc[2][2];
+    // Scores of my tile: tokens 16 wave .. 16 wave + 15 of the stage.
+    const int tt = wave;
+    float xs[4];
+    if (16 * tt < valid) {
+      f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+      const int r = tt * 16 + ln;
+      const int sw = swz_ckv(r), swk = swz_kpe(r);
+      // Fragments are read six K-steps at a time, ahead of their MFMAs.
+      constexpr int KG = 6;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-      acc[mt][0] = acc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < KSTEPS; k0 += KG) {
+        vec8 kf[KG];
 #pragma unroll
-    for (int k = 0; k < KSTEPS; ++k) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int r = mt * 16 + ln;
-        const MLA_LDS char* pk;
-        if (k < LAT / 32) {
-          pk = stg + r * CKV_ROW + (((4 * k + lg) ^ swz_ckv(r)) * 16);
-        } else {
-          pk = stg + CKV_TILE + r * KPE_ROW + (((4 * (k - LAT / 32) + lg) ^ swz_kpe(r)) * 16);
+        for (int i = 0; i < KG; ++i) {
+          const int kk = k0 + i;
+          const MLA_LDS char* pk = (kk < LAT / 32)
+              ? stg + r * CKV_ROW + (((4 * kk + lg) ^ sw) * 16)
+              : stg + ST_KPE + r * KPE_ROW + (((4 * (kk - LAT / 32) + lg) ^ swk) * 16);
+          kf[i] = *(const MLA_LDS vec8*)pk;
         }
-        const vec8 kf = *(const MLA_LDS vec8*)pk;
-        acc[mt][k & 1] = E::mfma(kf, q[k], acc[mt][k & 1]);
+#pragma unroll
+        for (int i = 0; i < KG; ++i) {
+          if (i & 1) acc1 = E::mfma(kf[i], q[k0 + i], acc1);
+          else acc0 = E::mfma(kf[i], q[k0 + i], acc0);
+        }
       }
-    }
-    // Lane (ln, lg) now holds, for head head0+ln, the tokens
-    // 4*lg+j (j < 4, from M-tile 0) and 16+4*lg+(j-4) (j >= 4, M-tile 1).
-    float xs[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      xs[j] = (acc[0][0][j] + acc[0][1][j]) * c2;
-      xs[4 + j] = (acc[1][0][j] + acc[1][1][j]) * c2;
-    }
-    if (valid < BS) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int tk = (j < 4) ? (4 * lg + j) : (16 + 4 * lg + (j - 4));
-        if (tk >= valid) xs[j] = -INFINITY;
+      for (int j = 0; j < 4; ++j) {
+        const int tk = 16 * tt + 4 * lg + j;
+        xs[j] = (tk < valid) ? (acc0[j] + acc1[j]) * c2 : -INFINITY;
       }
-    }
-    float bm = xs[0];
+    } else {
 #pragma unroll
-    for (int j = 1; j < 8; ++j) bm = fmaxf(bm, xs[j]);
-    bm = fmaxf(bm, shfl_xor(bm, 16));
-    bm = fmaxf(bm, shfl_xor(bm, 32));
+      for (int j = 0; j < 4; ++j) xs[j] = -INFINITY;
+    }
+    float tm = fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3]));
+    tm = fmaxf(tm, shfl_xor(tm, 16));
+    tm = fmaxf(tm, shfl_xor(tm, 32));
+    if (lg == 0) max_lds[wave * HG + ln] = tm;
+    bump_counter(maxed, lane);
+    wait_counter(maxed, CWAVES * (k + 1));
+    float bm = max_lds[ln];
+#pragma unroll
+    for (int w = 1; w < CWAVES; ++w) bm = fmaxf(bm, max_lds[w * HG + ln]);
+    // Every compute wave takes the same decision from the same values.
     const bool need = bm > m_ref + RESCALE_LOG2;
     if (__any(need)) {
       const float m_new = need ? bm : m_ref;
@@ -346,61 +373,80 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(PartitionArgs a) {
       l_part *= alpha;
       m_ref = m_new;
     }
-    vec8 pv;
+    {
+      // My tile is half of the B operand of value K-step tt / 2: tokens
+      // 32 kb + 4 lg + j fill slots j < 4 (even tile), 32 kb + 16 + 4 lg + j
+      // slots j >= 4 (odd tile). Masked tokens give exactly 0, so a tile
+      // past the context end still writes its (zero) half.
+      vec4 pv;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const typename E::scalar pj =
-          static_cast<typename E::scalar>(__builtin_amdgcn_exp2f(xs[j] - m_ref));
-      pv[j] = pj;
-      l_part += static_cast<float>(pj);
+      for (int j = 0; j < 4; ++j) {
+        const scalar pj = static_cast<scalar>(__builtin_amdgcn_exp2f(xs[j] - m_ref));
+        pv[j] = pj;
+        l_part += static_cast<float>(pj);
+      }
+      *(MLA_LDS vec4*)(smem + XP + ((tt >> 1) * 64 + lane) * 16 + (tt & 1) * 8) = pv;
     }
-
-    // Values: O^T[dims, heads] += V^T[dims, tokens] . P^T[tokens, heads].
-    // The A operand of lane (ln, lg) is dim 16*dtg+ln of tokens
-    // 4*lg..4*lg+3 and 16+4*lg..16+4*lg+3, read transposed from the tile.
+    bump_counter(probs, lane);
+    wait_counter(probs, CWAVES * (k + 1));
+    // Values, K-step kb = tokens 32 kb .. 32 kb + 31; the A operand of lane
+    // (ln, lg) is dim 16 dtg + ln of tokens 32 kb + 4 lg + j and
+    // 32 kb + 16 + 4 lg + j (j < 4), read transposed from the tile.
+    const int ksteps_pv = valid > BS ? 2 : 1;
 #pragma unroll
-    for (int dt = 0; dt < DT_PER_WAVE; ++dt) {
-      const int dtg = wave * DT_PER_WAVE + dt;
-      const int r1 = 4 * lg + (ln >> 2);
-      const int r2 = r1 + 16;
-      const int cpos = 2 * dtg + ((ln >> 1) & 1);   // 16-byte chunk holding my dims
-      const int half = (ln & 1) * 8;
-      const vec4 v1 = E::tr_read(stg + r1 * CKV_ROW + ((cpos ^ swz_ckv(r1)) * 16) + half);
-      const vec4 v2 = E::tr_read(stg + r2 * CKV_ROW + ((cpos ^ swz_ckv(r2)) * 16) + half);
-      const vec8 vf = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
-      o[dt] = E::mfma(vf, pv, o[dt]);
+    for (int kb = 0; kb < 2; ++kb) {
+      if (kb < ksteps_pv) {
+        const vec8 pv = *(const MLA_LDS vec8*)(smem + XP + (kb * 64 + lane) * 16);
+        const int r1 = kb * BS + 4 * lg + (ln >> 2);
+        const int r2 = r1 + 16;
+        const MLA_LDS char* v1row = stg + r1 * CKV_ROW + (ln & 1) * 8;
+        const MLA_LDS char* v2row = stg + r2 * CKV_ROW + (ln & 1) * 8;
+        const int s1 = swz_ckv(r1), s2 = swz_ckv(r2);
+#pragma unroll
+        for (int dt = 0; dt < DT_PER_WAVE; ++dt) {
+          const int dtg = wave * DT_PER_WAVE + dt;
+          const int cpos = 2 * dtg + ((ln >> 1) & 1);
+          const vec4 v1 = E::tr_read(v1row + ((cpos ^ s1) * 16));
+          const vec4 v2 = E::tr_read(v2row + ((cpos ^ s2) * 16));
+          o[dt] = E::mfma(__builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7), pv, o[dt]);
+        }
+      }
     }
-
-    __syncthreads();   // this stage is free again
-    if (more) {
-      issue_block(a, next_phys, lds0 + st * STAGE, wave, lane);
-      ++issued;
-    }
+    bump_counter(freed + slot, lane);
   }
 
-  // ---- epilogue: normalise and write --------------------------------------
-  float l_tot = l_part + shfl_xor(l_part, 16);
-  l_tot = l_tot + shfl_xor(l_tot, 32);
+  // ---- epilogue: normalise and write -------------------------------------
+  // Sum the four tiles' shares of l (fixed order), through the maxima area:
+  // every wave has read the last maxima before anyone passes `probs`.
+  {
+    float l_w = l_part + shfl_xor(l_part, 16);
+    l_w = l_w + shfl_xor(l_w, 32);
+    if (lg == 0) max_lds[wave * HG + ln] = l_w;
+  }
+  bump_counter(maxed, lane);
+  wait_counter(maxed, CWAVES * (nst + 1));
+  float l_tot = max_lds[ln];
+#pragma unroll
+  for (int w = 1; w < CWAVES; ++w) l_tot += max_lds[w * HG + ln];
   const float inv = 1.0f / l_tot;
-  const float lse2 = m_ref + __builtin_amdgcn_logf(l_tot);
 #pragma unroll
   for (int dt = 0; dt < DT_PER_WAVE; ++dt) {
     const int d0 = (wave * DT_PER_WAVE + dt) * 16 + lg * 4;
     const f32x4 v = o[dt] * inv;
-    if (a.direct) {
-      uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) +
-                      ((int64_t)b * a.heads + my_head) * LAT + d0;
-      typename E::vec4 h;
+    if (direct) {
+      uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)b * a.heads + my_head) * LAT + d0;
+      vec4 hv;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) h[j] = static_cast<typename E::scalar>(v[j]);
-      *reinterpret_cast<typename E::vec4*>(dst) = h;
+      for (int j = 0; j < 4; ++j) hv[j] = static_cast<scalar>(v[j]);
+      *reinterpret_cast<vec4*>(dst) = hv;
     } else {
       float* dst = a.partial_out + ((int64_t)row * a.heads + my_head) * LAT + d0;
       *reinterpret_cast<f32x4*>(dst) = v;
     }
   }
   if (wave == 0 && lg == 0) {
-    if (a.direct) {
+    const float lse2 = m_ref + __builtin_amdgcn_logf(l_tot);
+    if (direct) {
       if (a.lse2_out) a.lse2_out[(int64_t)b * a.heads + my_head] = lse2;
     } else {
       a.partial_lse2[(int64_t)row * a.heads + my_head] = lse2;
@@ -480,35 +526,29 @@ extern "C" int mla_decode_partition(
   a.q_pe = static_cast<const uint16_t*>(q_pe);
   a.ckv = static_cast<const uint16_t*>(ckv_cache);
   a.kpe = static_cast<const uint16_t*>(kpe_cache);
-  a.block_table = block_table;
-  a.context_lens = context_lens;
-  a.partitions = partitions;
-  a.splits = splits;
-  a.row_indptr = row_indptr;
   a.partial_out = partial_out;
   a.partial_lse2 = partial_lse2;
   a.out = out;
   a.lse2_out = lse2_out;
   a.debug_ranges = debug_ranges;
   a.num_blocks = num_blocks;
-  a.max_blocks = max_blocks_per_seq;
-  a.batch = batch;
   a.heads = num_heads;
-  a.groups = num_heads / HG;
-  a.rows_per_req = direct ? 1 : max_rows_per_req;
-  a.direct = direct ? 1 : 0;
-  a.total_rows = total_rows;
   a.scale_log2 = scale * 1.4426950408889634f;
+  const int32_t groups = num_heads / HG;
+  const int32_t rows_per_req = direct ? 1 : max_rows_per_req;
 
-  const int64_t slots = (int64_t)batch * a.rows_per_req;
-  const int64_t wgs = ((slots + 7) / 8) * 8 * a.groups;
+  const int64_t slots = (int64_t)batch * rows_per_req;
+  const int64_t wgs = ((slots + 7) / 8) * 8 * groups;
   if (wgs > INT32_MAX || slots > INT32_MAX)
     return fail(MLA_E_SHAPE, "grid too large (%lld workgroups)", (long long)wgs);
-  a.slots = (int32_t)slots;
   if (dtype == MLA_F16)
-    hipLaunchKernelGGL(partition_kernel<0>, dim3((unsigned)wgs), dim3(THREADS), 0, stream, a);
+    hipLaunchKernelGGL(partition_kernel<0>, dim3((unsigned)wgs), dim3(THREADS), 0, stream, groups,
+                       rows_per_req, (int32_t)slots, direct ? 1 : 0, total_rows, max_blocks_per_seq,
+                       context_lens, row_indptr, partitions, splits, block_table, a);
   else
-    hipLaunchKernelGGL(partition_kernel<1>, dim3((unsigned)wgs), dim3(THREADS), 0, stream, a);
+    hipLaunchKernelGGL(partition_kernel<1>, dim3((unsigned)wgs), dim3(THREADS), 0, stream, groups,
+                       rows_per_req, (int32_t)slots, direct ? 1 : 0, total_rows, max_blocks_per_seq,
+                       context_lens, row_indptr, partitions, splits, block_table, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(MLA_E_HIP, "partition launch: %s", hipGetErrorString(e));
   count(direct ? 0 : 1, 1);

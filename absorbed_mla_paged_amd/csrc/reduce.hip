@@ -9,11 +9,12 @@
 // "How #898's merge kernel is reused"; zero weight for rows with no visible
 // key and a single rounding after the merge per MTPLX pull request 639.)
 //
-// One workgroup handles (b, h, a 64-dim slice): 16 row lanes x 16 threads,
+// One workgroup handles (b, h, a 32-dim slice): 32 row lanes x 8 threads,
 // each thread owning 4 consecutive dims (one 16-byte load per row), so a
-// row's slice is one 256-byte segment. Row lane k takes rows k, k+16, ...
-// in order; the 16 partial sums are then added in a fixed order, so the
-// result is bit-identical run to run.
+// row's slice is one 128-byte line. Row lane k takes rows k, k+32, ... in
+// order, with 8 rows' loads issued before any is used, so a request's whole
+// partial set is in flight at once; the 32 row-lane sums are then added in a
+// fixed order, so the result is bit-identical run to run.
 #include "device_common.h"
 #include "internal.h"
 
@@ -25,11 +26,12 @@ namespace {
 using namespace dev;
 
 constexpr int LAT = MLA_KV_LORA_RANK;
-constexpr int SLICE = 64;                 // dims per workgroup
-constexpr int SLICES = LAT / SLICE;       // 8
-constexpr int TPR = SLICE / 4;            // threads per row: 16
-constexpr int RL = 16;                    // row lanes
+constexpr int SLICE = 32;                 // dims per workgroup
+constexpr int SLICES = LAT / SLICE;       // 16
+constexpr int TPR = SLICE / 4;            // threads per row: 8
+constexpr int RL = 32;                    // row lanes
 constexpr int THREADS = TPR * RL;         // 256
+constexpr int UNROLL = 8;                 // rows in flight per thread
 
 struct ReduceArgs {
   const float* partial_out;
@@ -111,11 +113,20 @@ __global__ __launch_bounds__(THREADS) void reduce_kernel(ReduceArgs a) {
   for (int w = 1; w < THREADS / 64; ++w) W += red[w];
 
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int r = rl; r < nr; r += RL) {
-    const int64_t row = r0 + r;
-    const float wr = __builtin_amdgcn_exp2f(a.partial_lse2[row * a.heads + h] - M);
-    const f32x4 v = *reinterpret_cast<const f32x4*>(a.partial_out + (row * a.heads + h) * LAT + d0);
-    acc += wr * v;
+  for (int rb = rl; rb < nr; rb += RL * UNROLL) {
+    f32x4 v[UNROLL];
+    float lw[UNROLL];
+#pragma unroll
+    for (int j = 0; j < UNROLL; ++j) {
+      const int r = rb + j * RL;
+      const int64_t row = r0 + min(r, nr - 1);
+      lw[j] = a.partial_lse2[row * a.heads + h];
+      v[j] = *reinterpret_cast<const f32x4*>(a.partial_out + (row * a.heads + h) * LAT + d0);
+    }
+#pragma unroll
+    for (int j = 0; j < UNROLL; ++j) {
+      if (rb + j * RL < nr) acc += __builtin_amdgcn_exp2f(lw[j] - M) * v[j];
+    }
   }
   part[rl][c4] = acc;
   __syncthreads();
