@@ -26,12 +26,15 @@
 //  * Scores: S^T[token, head] = K[token, :] . Q^T[:, head] on
 //    v_mfma_f32_16x16x32 (K = 576 = 18 steps); compute wave w scores the
 //    stage's 16-token tile w. Q (16 x 576) sits in their registers.
-//  * Online softmax in the base-2 domain: the tile maxima of each head meet
-//    in LDS; the running maximum only moves when a stage beats it by more
-//    than 2^8, so rescaling is rare. Each compute wave writes its tile's
-//    probabilities to LDS in the B-operand layout of the value product. The
-//    compute waves meet through LDS counters as well (never s_barrier, which
-//    would also wait for the copy waves).
+//  * Online softmax in the base-2 domain: each compute wave writes its raw
+//    score tile to LDS and, after one meeting point per stage, reads all four
+//    back. The MFMA output layout is the same in every wave, so lane (ln, lg)
+//    reads exactly the 16 scores it needs: head ln at tokens 16 t + 4 lg + j,
+//    which is also the B-operand layout of the value product. Every compute
+//    wave then takes the same maximum, probabilities and running sum itself.
+//    The running maximum only moves when a stage beats it by more than 2^8,
+//    so rescaling is rare. The compute waves meet through an LDS counter
+//    (never s_barrier, which would also wait for the copy waves).
 //  * Values: O^T[dim, head] += V^T[dim, token] . P^T[token, head] on
 //    v_mfma_f32_16x16x32; V^T is read from the same LDS tile with
 //    ds_read_b64_tr_b16. Compute wave w owns dims [128 w, 128 w + 128).
@@ -60,12 +63,11 @@ constexpr int KSTEPS = (LAT + ROPE) / 32;       // 18 score K-steps
 constexpr int DT_PER_WAVE = LAT / 16 / CWAVES;  // 8 output dim tiles per wave
 constexpr int OPS_PER_COPY = STAGE / 1024 / 2;  // 36 copies per copy wave
 constexpr float RESCALE_LOG2 = 8.0f;            // lazy-rescale threshold
-// After the two slots: counters ready[2], free[2], issued, maxima, probs;
-// the tile maxima [4][16]; the P fragments [2 K-steps][64 lanes][16 B].
+// After the two slots: counters ready[2], free[2], issued, scored; then the
+// score tiles [2 parities][4 tiles][64 lanes][16 B].
 constexpr int XCNT = 2 * STAGE;
-constexpr int XMAX = XCNT + 64;
-constexpr int XP = XMAX + CWAVES * HG * 4;
-constexpr int LDS_BYTES = XP + 2 * 64 * 16;
+constexpr int XS = XCNT + 64;
+constexpr int LDS_BYTES = XS + 2 * CWAVES * 64 * 16;
 static_assert(OPS_PER_COPY * 2 * 1024 == STAGE, "stage split");
 static_assert(OPS_PER_COPY < 64, "vmcnt range");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -234,9 +236,8 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
   MLA_LDS uint32_t* ready = (MLA_LDS uint32_t*)(smem + XCNT);
   MLA_LDS uint32_t* freed = ready + 2;
   MLA_LDS uint32_t* issued = ready + 4;
-  MLA_LDS uint32_t* maxed = ready + 5;   // compute waves: maxima written
-  MLA_LDS uint32_t* probs = ready + 6;   // compute waves: P written
-  if (tid < 7) ready[tid] = 0u;
+  MLA_LDS uint32_t* scored = ready + 5;  // compute waves: score tiles written
+  if (tid < 6) ready[tid] = 0u;
   __syncthreads();
 
   if (copier) {
@@ -309,9 +310,8 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
 #pragma unroll
   for (int dt = 0; dt < DT_PER_WAVE; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY;  // reference maximum of my head, base 2
-  float l_part = 0.f;       // my tile's share of the running sum
+  float l_part = 0.f;       // this lane's 16 token slots of the running sum
   const float c2 = a.scale_log2;
-  MLA_LDS float* max_lds = (MLA_LDS float*)(smem + XMAX);
 
   for (int k = 0; k < nst; ++k) {
     const int slot = k & 1;
@@ -354,16 +354,23 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) xs[j] = -INFINITY;
     }
-    float tm = fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3]));
-    tm = fmaxf(tm, shfl_xor(tm, 16));
-    tm = fmaxf(tm, shfl_xor(tm, 32));
-    if (lg == 0) max_lds[wave * HG + ln] = tm;
-    bump_counter(maxed, lane);
-    wait_counter(maxed, CWAVES * (k + 1));
-    float bm = max_lds[ln];
+    // Publish my tile, meet, read all four tiles (same lane, same layout).
+    MLA_LDS char* sbuf = smem + XS + (k & 1) * (CWAVES * 64 * 16);
+    *(MLA_LDS f32x4*)(sbuf + (tt * 64 + lane) * 16) = f32x4{xs[0], xs[1], xs[2], xs[3]};
+    bump_counter(scored, lane);
+    wait_counter(scored, CWAVES * (k + 1));
+    float sc[16];
 #pragma unroll
-    for (int w = 1; w < CWAVES; ++w) bm = fmaxf(bm, max_lds[w * HG + ln]);
-    // Every compute wave takes the same decision from the same values.
+    for (int t = 0; t < CWAVES; ++t) {
+      const f32x4 v = *(const MLA_LDS f32x4*)(sbuf + (t * 64 + lane) * 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sc[4 * t + j] = v[j];
+    }
+    float bm = sc[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) bm = fmaxf(bm, sc[j]);
+    bm = fmaxf(bm, shfl_xor(bm, 16));
+    bm = fmaxf(bm, shfl_xor(bm, 32));
     const bool need = bm > m_ref + RESCALE_LOG2;
     if (__any(need)) {
       const float m_new = need ? bm : m_ref;
@@ -373,30 +380,22 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
       l_part *= alpha;
       m_ref = m_new;
     }
-    {
-      // My tile is half of the B operand of value K-step tt / 2: tokens
-      // 32 kb + 4 lg + j fill slots j < 4 (even tile), 32 kb + 16 + 4 lg + j
-      // slots j >= 4 (odd tile). Masked tokens give exactly 0, so a tile
-      // past the context end still writes its (zero) half.
-      vec4 pv;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const scalar pj = static_cast<scalar>(__builtin_amdgcn_exp2f(xs[j] - m_ref));
-        pv[j] = pj;
-        l_part += static_cast<float>(pj);
-      }
-      *(MLA_LDS vec4*)(smem + XP + ((tt >> 1) * 64 + lane) * 16 + (tt & 1) * 8) = pv;
-    }
-    bump_counter(probs, lane);
-    wait_counter(probs, CWAVES * (k + 1));
-    // Values, K-step kb = tokens 32 kb .. 32 kb + 31; the A operand of lane
-    // (ln, lg) is dim 16 dtg + ln of tokens 32 kb + 4 lg + j and
-    // 32 kb + 16 + 4 lg + j (j < 4), read transposed from the tile.
+    // Values, K-step kb = tokens 32 kb .. 32 kb + 31. The B operand of lane
+    // (ln, lg) is P of head ln at tokens 32 kb + 4 lg + j and
+    // 32 kb + 16 + 4 lg + j (j < 4): scores sc[8 kb + j]. The A operand is
+    // dim 16 dtg + ln of the same tokens, read transposed from the tile.
+    // Masked tokens give p = 0 exactly.
     const int ksteps_pv = valid > BS ? 2 : 1;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if (kb < ksteps_pv) {
-        const vec8 pv = *(const MLA_LDS vec8*)(smem + XP + (kb * 64 + lane) * 16);
+        vec8 pv;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const scalar pj = static_cast<scalar>(__builtin_amdgcn_exp2f(sc[8 * kb + j] - m_ref));
+          pv[j] = pj;
+          l_part += static_cast<float>(pj);
+        }
         const int r1 = kb * BS + 4 * lg + (ln >> 2);
         const int r2 = r1 + 16;
         const MLA_LDS char* v1row = stg + r1 * CKV_ROW + (ln & 1) * 8;
@@ -416,18 +415,8 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
   }
 
   // ---- epilogue: normalise and write -------------------------------------
-  // Sum the four tiles' shares of l (fixed order), through the maxima area:
-  // every wave has read the last maxima before anyone passes `probs`.
-  {
-    float l_w = l_part + shfl_xor(l_part, 16);
-    l_w = l_w + shfl_xor(l_w, 32);
-    if (lg == 0) max_lds[wave * HG + ln] = l_w;
-  }
-  bump_counter(maxed, lane);
-  wait_counter(maxed, CWAVES * (nst + 1));
-  float l_tot = max_lds[ln];
-#pragma unroll
-  for (int w = 1; w < CWAVES; ++w) l_tot += max_lds[w * HG + ln];
+  float l_tot = l_part + shfl_xor(l_part, 16);
+  l_tot = l_tot + shfl_xor(l_tot, 32);
   const float inv = 1.0f / l_tot;
 #pragma unroll
   for (int dt = 0; dt < DT_PER_WAVE; ++dt) {
