@@ -14,8 +14,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla_decode.so")
-SOURCES = ["plan.cpp", "partition.hip", "reduce.hip"]
-HEADERS = ["internal.h", "device_common.h"]
+SOURCES = ["plan.cpp", "partition.hip", "partition_wide.hip", "reduce.hip"]
+HEADERS = ["internal.h", "device_common.h", "partition_common.h"]
 
 
 def hipcc() -> str:

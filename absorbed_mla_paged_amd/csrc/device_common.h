@@ -84,7 +84,46 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
       : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
       : "memory", "m0");
 }
+
+// Same copy with a wave-uniform 64-bit global base in SGPRs and a 32-bit
+// per-lane byte offset (global_load_lds_dwordx4 v_off, s_base): no 64-bit
+// per-lane address arithmetic or registers.
+__device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory", "m0");
+}
 #pragma clang diagnostic pop
+
+// LDS reads issued from inline assembly, for loops that keep several reads
+// in flight ahead of the MFMAs consuming them (the compiler's own schedule
+// keeps one or two). The compiler does not count these reads, so every use
+// must be preceded by lds_wait<N>(value), N = the number of LDS reads issued
+// after this one. LDS operations complete in order; any other LDS or scalar
+// operation the compiler puts in between only makes such a wait stricter.
+template <typename T>
+__device__ __forceinline__ T lds_read_b128(uint32_t addr) {
+  T v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+__device__ __forceinline__ u32x2 lds_read_tr_b16(uint32_t addr) {
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+// Wait until at most N LDS operations are outstanding; `v` (the value the
+// caller waits for) is routed through the statement so that its uses
+// cannot be scheduled above it.
+template <int N, typename T>
+__device__ __forceinline__ void lds_wait(T& v) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt field is 4 bits");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(N));
+}
 
 // Read-only int32 metadata (block table, plan arrays) through the constant
 // address space: uniform loads then become scalar (s_load, counted by

@@ -38,8 +38,7 @@
 //  * Values: O^T[dim, head] += V^T[dim, token] . P^T[token, head] on
 //    v_mfma_f32_16x16x32; V^T is read from the same LDS tile with
 //    ds_read_b64_tr_b16. Compute wave w owns dims [128 w, 128 w + 128).
-#include "device_common.h"
-#include "internal.h"
+#include "partition_common.h"
 
 #include <cmath>
 
@@ -47,22 +46,16 @@ namespace mla {
 namespace {
 
 using namespace dev;
+using namespace part;
 
-constexpr int BS = MLA_BLOCK_SIZE;              // tokens per cache block
-constexpr int LAT = MLA_KV_LORA_RANK;           // 512
-constexpr int ROPE = MLA_ROPE_DIM;              // 64
-constexpr int CKV_ROW = LAT * 2;                // bytes per ckv row
-constexpr int KPE_ROW = ROPE * 2;               // bytes per kpe row
 constexpr int ST_TOK = 2 * BS;                  // tokens per stage
 constexpr int ST_KPE = ST_TOK * CKV_ROW;        // kpe rows after the ckv rows
 constexpr int STAGE = ST_TOK * (CKV_ROW + KPE_ROW);   // 72 KB
 constexpr int CWAVES = 4;                       // compute waves
 constexpr int THREADS = 64 * 2 * CWAVES;        // plus as many copy waves
 constexpr int HG = 16;                          // heads per workgroup
-constexpr int KSTEPS = (LAT + ROPE) / 32;       // 18 score K-steps
 constexpr int DT_PER_WAVE = LAT / 16 / CWAVES;  // 8 output dim tiles per wave
 constexpr int OPS_PER_COPY = STAGE / 1024 / 2;  // 36 copies per copy wave
-constexpr float RESCALE_LOG2 = 8.0f;            // lazy-rescale threshold
 // After the two slots: counters ready[2], free[2], issued, scored; then the
 // score tiles [2 parities][4 tiles][64 lanes][16 B].
 constexpr int XCNT = 2 * STAGE;
@@ -72,58 +65,9 @@ static_assert(OPS_PER_COPY * 2 * 1024 == STAGE, "stage split");
 static_assert(OPS_PER_COPY < 64, "vmcnt range");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
-// Arguments the start of every workgroup waits on. They are passed as the
-// first kernel arguments (16 dwords), which gfx950 preloads into SGPRs at
-// wave launch, so finding the row costs no argument fetch.
-struct RowArgs {
-  int32_t groups;        // heads / HG
-  int32_t rows_per_req;  // grid rows per request (max_rows_per_req)
-  int32_t slots;         // batch * rows_per_req
-  int32_t direct;        // 1: one row per request, write `out`
-  int32_t total_rows;
-  int32_t max_blocks;
-  const int32_t* context_lens;
-  const int32_t* row_indptr;
-  const int32_t* partitions;
-  const int32_t* splits;
-  const int32_t* block_table;
-};
-
-// The rest, fetched from the argument segment while the row is looked up.
-struct PartitionArgs {
-  const uint16_t* q_absorbed;
-  const uint16_t* q_pe;
-  const uint16_t* ckv;
-  const uint16_t* kpe;
-  float* partial_out;
-  float* partial_lse2;
-  void* out;
-  float* lse2_out;
-  int32_t* debug_ranges;
-  int32_t num_blocks;
-  int32_t heads;
-  float scale_log2;      // scale * log2(e)
-};
-
-// XOR swizzles of the 16-byte chunk index inside an LDS row.
-__device__ __forceinline__ int swz_ckv(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
-__device__ __forceinline__ int swz_kpe(int r) { return (r >> 1) & 7; }
-
-__device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
-
-// Spin until the LDS counter reaches `target` (the waves of a workgroup are
-// all resident, and every counter a wave waits on is bumped by waves that do
-// not wait on this one first, so the wait ends).
-__device__ __forceinline__ void wait_counter(const MLA_LDS uint32_t* c, uint32_t target) {
-  while (*(const volatile MLA_LDS uint32_t*)c < target) __builtin_amdgcn_s_sleep(1);
-  asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ void bump_counter(MLA_LDS uint32_t* c, int lane) {
-  wait_lgkmcnt0();   // this wave's LDS reads / writes before the bump are done
-  if (lane == 0) __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-
+// The leading scalar kernel arguments (16 dwords, up to block_table) are
+// preloaded into SGPRs at wave launch on gfx950, so finding the row costs
+// no argument fetch; the PartitionArgs block is fetched meanwhile.
 template <int DT>
 __global__ __launch_bounds__(THREADS) void partition_kernel(
     int32_t groups, int32_t rows_per_req, int32_t slots, int32_t direct, int32_t total_rows,
@@ -480,8 +424,9 @@ extern "C" int mla_decode_partition(
                 num_heads);
   if (dtype != MLA_F16 && dtype != MLA_BF16) return fail(MLA_E_UNSUPPORTED, "dtype %d", dtype);
   const int32_t hpw = heads_per_wg ? heads_per_wg : default_heads_per_wg(num_heads);
-  if (hpw != HG || num_heads % hpw)
-    return fail(MLA_E_UNSUPPORTED, "heads_per_wg %d (this build has 16-head workgroups)", hpw);
+  if (!valid_heads_per_wg(num_heads, hpw))
+    return fail(MLA_E_UNSUPPORTED, "heads_per_wg %d for %d heads (16, 64 or 128 dividing it)",
+                hpw, num_heads);
   if (!std::isfinite(scale)) return fail(MLA_E_RANGE, "scale is not finite");
   if (batch == 0) return MLA_OK;
   if (!q_absorbed || !q_pe || !ckv_cache || !kpe_cache || !block_table || !context_lens)
@@ -510,7 +455,7 @@ extern "C" int mla_decode_partition(
       (debug_ranges && !aligned(debug_ranges, 8)))
     return fail(MLA_E_ALIGN, "int32/fp32 arrays misaligned");
 
-  PartitionArgs a;
+  part::PartitionArgs a;
   a.q_absorbed = static_cast<const uint16_t*>(q_absorbed);
   a.q_pe = static_cast<const uint16_t*>(q_pe);
   a.ckv = static_cast<const uint16_t*>(ckv_cache);
@@ -523,14 +468,18 @@ extern "C" int mla_decode_partition(
   a.num_blocks = num_blocks;
   a.heads = num_heads;
   a.scale_log2 = scale * 1.4426950408889634f;
-  const int32_t groups = num_heads / HG;
+  const int32_t groups = num_heads / hpw;
   const int32_t rows_per_req = direct ? 1 : max_rows_per_req;
 
   const int64_t slots = (int64_t)batch * rows_per_req;
   const int64_t wgs = ((slots + 7) / 8) * 8 * groups;
   if (wgs > INT32_MAX || slots > INT32_MAX)
     return fail(MLA_E_SHAPE, "grid too large (%lld workgroups)", (long long)wgs);
-  if (dtype == MLA_F16)
+  if (hpw != HG)
+    part::launch_wide(dtype, hpw, (unsigned)wgs, stream, groups, rows_per_req, (int32_t)slots,
+                      direct ? 1 : 0, total_rows, max_blocks_per_seq, context_lens, row_indptr,
+                      partitions, splits, block_table, a);
+  else if (dtype == MLA_F16)
     hipLaunchKernelGGL(partition_kernel<0>, dim3((unsigned)wgs), dim3(THREADS), 0, stream, groups,
                        rows_per_req, (int32_t)slots, direct ? 1 : 0, total_rows, max_blocks_per_seq,
                        context_lens, row_indptr, partitions, splits, block_table, a);

@@ -1,0 +1,135 @@
+// Pieces shared by the two partition kernels (16-head and wide workgroups):
+// the argument block, the swizzles of the LDS tiles, the row lookup with the
+// partition/tile index math, and the launch entry of the wide kernel.
+#pragma once
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace mla {
+namespace part {
+
+// Arguments not needed before the row is known (fetched from the kernel
+// argument segment while the row metadata is in flight).
+struct PartitionArgs {
+  const uint16_t* q_absorbed;
+  const uint16_t* q_pe;
+  const uint16_t* ckv;
+  const uint16_t* kpe;
+  float* partial_out;
+  float* partial_lse2;
+  void* out;
+  float* lse2_out;
+  int32_t* debug_ranges;
+  int32_t num_blocks;
+  int32_t heads;
+  float scale_log2;  // scale * log2(e)
+};
+
+constexpr int BS = MLA_BLOCK_SIZE;      // tokens per cache block
+constexpr int LAT = MLA_KV_LORA_RANK;   // 512
+constexpr int ROPE = MLA_ROPE_DIM;      // 64
+constexpr int CKV_ROW = LAT * 2;        // bytes per ckv row
+constexpr int KPE_ROW = ROPE * 2;       // bytes per kpe row
+constexpr int KSTEPS = (LAT + ROPE) / 32;  // 18 score K-steps of 32
+constexpr float RESCALE_LOG2 = 8.0f;    // lazy-rescale threshold (base 2)
+
+#ifdef __HIPCC__
+// XOR swizzles of the 16-byte chunk index inside an LDS row: ckv rows hold
+// 64 chunks (the low 4 bits are permuted), kpe rows 8.
+__device__ __forceinline__ int swz_ckv(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_kpe(int r) { return (r >> 1) & 7; }
+
+__device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// One workgroup's row: request b, its token range and blocks.
+struct RowInfo {
+  int b;        // request
+  int row;      // partial row (request b when the launch is single pass)
+  int hg;       // head group
+  int tok_lo, tok_hi;
+  int blk_lo;   // first block of the range (request-local)
+  int nblocks;  // blocks holding at least one visible token
+};
+
+// Which (request, local row, head group) workgroup L owns. Workgroups are
+// dealt to the 8 XCDs round-robin by linear id; slot u = b * rows_per_req +
+// x, and the id layout L = ((u / 8) * G + hg) * 8 + u % 8 keeps the G head
+// groups of one row on one XCD, so they share its L2. Returns false for a
+// workgroup with nothing to do (grid padding, or x past the request's rows).
+__device__ __forceinline__ bool slot_of(int L, int groups, int rows_per_req, int slots,
+                                        int* b, int* x, int* hg) {
+  const int sl = L >> 3;
+  *hg = sl % groups;
+  const int u = (sl / groups) * 8 + (L & 7);
+  if (u >= slots) return false;
+  *b = u / rows_per_req;
+  *x = u % rows_per_req;
+  return true;
+}
+
+// Row metadata in one round of scalar loads, then the index math of
+// mla_partition_range (must agree with it bit for bit).
+__device__ __forceinline__ bool find_row(int b, int x, int direct, int total_rows,
+                                         int max_blocks, const int32_t* context_lens,
+                                         const int32_t* row_indptr,
+                                         const int32_t* partitions, const int32_t* splits,
+                                         RowInfo* ri) {
+  using dev::load_const;
+  int n = load_const(context_lens, b);
+  int P = 1, S = 1, row = b, nrows = 1;
+  if (!direct) {
+    const int r0 = load_const(row_indptr, b);
+    const int r1 = load_const(row_indptr, b + 1);
+    const int pv = load_const(partitions, b);
+    const int sv = load_const(splits, b);
+    nrows = r1 - r0;
+    P = max(1, min(pv, 1 << 25));
+    S = max(1, min(sv, 1 << 25));
+    row = r0 + x;
+  }
+  n = max(0, min(n, max_blocks * BS));
+  if (x >= nrows || row < 0 || row >= total_rows) return false;
+  const int p = x / S;
+  const int s = x % S;
+  const int nblk = cdiv(n, BS);
+  const int bpp = cdiv(nblk, P);
+  const int pb0 = min(p * bpp, nblk);
+  const int pb1 = min((p + 1) * bpp, nblk);
+  const int m = pb1 - pb0;
+  const int bps = m > 0 ? cdiv(m, S) : 0;
+  const int blk_lo = (p < P) ? pb0 + min(s * bps, m) : nblk;
+  const int blk_hi = (p < P) ? pb0 + min((s + 1) * bps, m) : nblk;
+  ri->b = b;
+  ri->row = row;
+  ri->tok_lo = min(blk_lo * BS, n);
+  ri->tok_hi = min(blk_hi * BS, n);
+  ri->blk_lo = blk_lo;
+  ri->nblocks = cdiv(ri->tok_hi - ri->tok_lo, BS);
+  return true;
+}
+
+// Spin until the LDS counter reaches `target`. Every counter a wave waits on
+// is bumped by waves of the same (resident) workgroup that do not first
+// wait on this one, so the wait ends.
+__device__ __forceinline__ void wait_counter(const MLA_LDS uint32_t* c, uint32_t target) {
+  while (*(const volatile MLA_LDS uint32_t*)c < target) __builtin_amdgcn_s_sleep(1);
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void bump_counter(MLA_LDS uint32_t* c, int lane) {
+  dev::wait_lgkmcnt0();  // this wave's LDS reads / writes before the bump are done
+  if (lane == 0) __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+#endif  // __HIPCC__
+
+// Launch of the wide kernel (heads_per_wg 64 or 128); arguments as the
+// 16-head kernel's. Host side, after the launcher's checks.
+void launch_wide(int dtype, int hpw, unsigned wgs, hipStream_t stream, int32_t groups,
+                 int32_t rows_per_req, int32_t slots, int32_t direct, int32_t total_rows,
+                 int32_t max_blocks, const int32_t* context_lens, const int32_t* row_indptr,
+                 const int32_t* partitions, const int32_t* splits, const int32_t* block_table,
+                 const PartitionArgs& a);
+
+}  // namespace part
+}  // namespace mla

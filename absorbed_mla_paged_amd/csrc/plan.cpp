@@ -41,12 +41,15 @@ void clear_error() { g_last_error.clear(); }
 void count(int which, uint64_t v) { g_counters[which].fetch_add(v, std::memory_order_relaxed); }
 
 int default_heads_per_wg(int32_t heads) {
-  (void)heads;
-  return 16;  // one 16-row MFMA tile of heads per workgroup
+  // 64 heads (two 32-head waves per token) wherever they divide H: the
+  // cache rows staged in LDS then feed 64 heads instead of 16, and the
+  // partial written per workgroup stays at a quarter of the 128-head one.
+  // Other head counts use one 16-row MFMA tile of heads per workgroup.
+  return heads % 64 == 0 ? 64 : 16;
 }
 
 bool valid_heads_per_wg(int32_t heads, int32_t hpw) {
-  return (hpw == 16 || hpw == 32 || hpw == 64 || hpw == 128) && heads % hpw == 0;
+  return (hpw == 16 || hpw == 64 || hpw == 128) && heads % hpw == 0;
 }
 
 TileRange tile_range(int64_t n, int32_t P, int32_t S, int32_t p, int32_t s) {
@@ -164,8 +167,31 @@ int mla_choose_partitions(int32_t batch, int32_t num_heads, int32_t q_len,
                                  prm.max_partitions);
       else P[b] = 1;
     }
-    tile = std::max<int64_t>(prm.min_tile_blocks,
-                             cdiv(G * total_blocks, num_cus * int64_t(prm.wgs_per_cu)));
+    const int64_t cap = num_cus * int64_t(prm.wgs_per_cu);
+    tile = std::max<int64_t>(prm.min_tile_blocks, cdiv(G * total_blocks, cap));
+    // Rounding each request's tiles up can still overshoot one wave of
+    // workgroups; then take the smallest larger tile whose grid fits (rows
+    // only shrink as the tile grows), or the one giving S_b = 1 everywhere.
+    auto grid_rows = [&](int64_t t) {
+      int64_t r = 0;
+      for (int32_t b = 0; b < batch; ++b)
+        r += P[b] * std::max<int64_t>(1, cdiv(cdiv(nblk[b], P[b]), t));
+      return r;
+    };
+    if (autoS && G * grid_rows(tile) > cap) {
+      int64_t hi = tile;
+      for (int32_t b = 0; b < batch; ++b) hi = std::max(hi, cdiv(nblk[b], P[b]));
+      if (G * grid_rows(hi) > cap) {
+        tile = hi;
+      } else {
+        int64_t lo = tile;  // grid_rows(lo) too many, grid_rows(hi) fits
+        while (hi - lo > 1) {
+          const int64_t mid = lo + (hi - lo) / 2;
+          if (G * grid_rows(mid) > cap) lo = mid; else hi = mid;
+        }
+        tile = hi;
+      }
+    }
     for (int32_t b = 0; b < batch; ++b) S[b] = autoS ? splits_for(nblk[b], P[b]) : prm.force_splits;
   }
 

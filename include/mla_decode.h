@@ -81,7 +81,9 @@ typedef struct {
   int32_t min_partitions;        /* lower clamp of the policy count (2) */
   int32_t max_partitions;        /* upper clamp, <= MLA_MAX_PARTITIONS (8) */
   int32_t num_cus;               /* compute units; 0 = ask the current device */
-  int32_t heads_per_wg;          /* heads per workgroup; 0 = library default */
+  int32_t heads_per_wg;          /* heads per workgroup: 16, 64 or 128 dividing
+                                    H; 0 = library default (64 if 64 divides
+                                    H, else 16) */
   int32_t min_tile_blocks;       /* smallest device tile in 32-token blocks (4) */
   int32_t wgs_per_cu;            /* device tiling target: workgroups per CU (1) */
   int32_t force_partitions;      /* >0: every request gets P_b = this */
@@ -117,8 +119,12 @@ void mla_default_plan_params(mla_plan_params* p);
  *   P_b = force_partitions, else clamp(ceil(n_b / tokens_per_partition),
  *         min_partitions, max_partitions) if eligible && n_b >= min_split_ctx,
  *         else 1
- *   tile = max(min_tile_blocks, ceil(G * sum nblk_b / (num_cus * wgs_per_cu)))
+ *   cap  = num_cus * wgs_per_cu
+ *   tile = max(min_tile_blocks, ceil(G * sum nblk_b / cap))
  *   S_b = force_splits, else max(1, ceil(ceil(nblk_b / P_b) / tile))
+ *   (auto S only) if G * sum P_b S_b > cap, tile becomes the smallest larger
+ *   value with G * sum P_b S_b <= cap, or max_b ceil(nblk_b / P_b) if none
+ *   fits, so the grid never spills into a second, nearly empty wave.
  * With q_len != 1 every request gets P_b = S_b = 1. If a workspace limit is
  * set and exceeded: double the tile until it fits or all S_b = 1 (auto S
  * only); then lower the largest P_b by one (lowest b first) down to 2; then

@@ -14,9 +14,12 @@ before the grid: the split path starts at 32K+ context). The rule:
   eligible   = q_len == 1 and B * G < num_cus  pure decode, small launch
   P_b        = force_P, else clamp(ceil(n_b / tokens_per_partition),
                min_P, max_P) if eligible and n_b >= min_split_ctx, else 1
-  tile       = max(min_tile_blocks,
-                   ceil(G * sum_b nblk_b / (num_cus * wgs_per_cu)))
+  cap        = num_cus * wgs_per_cu              workgroups in one wave
+  tile       = max(min_tile_blocks, ceil(G * sum_b nblk_b / cap))
   S_b        = force_S, else max(1, ceil(ceil(nblk_b / P_b) / tile))
+  fit        = (auto S only) if G * sum_b P_b * S_b > cap, the tile becomes
+               the smallest larger one with G * sum_b P_b * S_b <= cap, or,
+               if none fits, max_b ceil(nblk_b / P_b) (every S_b = 1)
   rows       = sum_b P_b * S_b, request-major (row_indptr)
   workspace  = rows * H * (512 + 1) * 4 bytes if any P_b * S_b > 1, else 0
 If q_len != 1 every request gets P_b = S_b = 1 (no split at all).
@@ -51,8 +54,8 @@ def _cdiv(a: int, b: int) -> int:
 
 def default_heads_per_wg(heads: int) -> int:
     """Heads one workgroup of the partition kernel covers (library default):
-    one 16-row MFMA tile of heads."""
-    return 16
+    64 when 64 divides the head count, else one 16-row MFMA tile."""
+    return 64 if heads % 64 == 0 else 16
 
 
 @dataclasses.dataclass
@@ -120,7 +123,7 @@ def choose_partitions(batch: int, heads: int, q_len: int, ctx, params: PlanParam
     if prm.workspace_limit_bytes < 0:
         raise ValueError("limit")
     hpw = prm.heads_per_wg or default_heads_per_wg(heads)
-    if hpw not in (16, 32, 64, 128) or heads % hpw:
+    if hpw not in (16, 64, 128) or heads % hpw:
         raise ValueError("heads per workgroup")
     G = heads // hpw
     nblk = [_cdiv(n, block_size) for n in ctx]
@@ -144,8 +147,26 @@ def choose_partitions(batch: int, heads: int, q_len: int, ctx, params: PlanParam
                              prm.max_partitions))
             else:
                 P.append(1)
-        tile = max(prm.min_tile_blocks,
-                   _cdiv(G * total_blocks, prm.num_cus * prm.wgs_per_cu))
+        cap = prm.num_cus * prm.wgs_per_cu
+        tile = max(prm.min_tile_blocks, _cdiv(G * total_blocks, cap))
+
+        def wgs(t):
+            return G * sum(p * _splits_for(nb, p, t) for nb, p in zip(nblk, P))
+
+        if autoS and wgs(tile) > cap:
+            biggest = max([tile] + [_cdiv(nb, p) for nb, p in zip(nblk, P)])
+            if wgs(biggest) > cap:
+                tile = biggest
+            else:
+                # wgs() never grows with the tile: bisect for the first fit.
+                bad, good = tile, biggest
+                while good - bad > 1:
+                    mid = (bad + good) // 2
+                    if wgs(mid) <= cap:
+                        good = mid
+                    else:
+                        bad = mid
+                tile = good
         S = [(_splits_for(nb, p, tile) if autoS else prm.force_splits)
              for nb, p in zip(nblk, P)]
 

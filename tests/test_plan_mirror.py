@@ -127,3 +127,41 @@ def test_exhaustive_small_grid_is_consistent():
         r = plan.choose_partitions(2, 32, 1, list(ctx), plan.PlanParams(num_cus=16))
         assert all(1 <= p <= 8 for p in r["P"]) and all(s >= 1 for s in r["S"])
         assert r["row_indptr"][-1] == sum(p * s for p, s in zip(r["P"], r["S"]))
+
+
+def test_device_tiling_fits_one_wave_81k_64_head_groups():
+    # 81920 tokens, P = 5 (512 blocks per partition), 128 heads in 64-head
+    # workgroups (G = 2): the first tile, ceil(2 * 2560 / 256) = 20 blocks,
+    # gives 5 * 26 rows = 260 workgroups, four past one wave of 256; 21
+    # blocks gives 5 * 25 rows = 250.
+    r = plan.choose_partitions(1, 128, 1, [81920], plan.PlanParams(num_cus=256))
+    assert r["heads_per_wg"] == 64 and r["groups"] == 2
+    assert r["P"] == [5] and r["tile_blocks"] == 21 and r["S"] == [25]
+    assert r["groups"] * r["total_rows"] == 250
+
+
+def test_device_tiling_fit_is_the_smallest_fitting_tile():
+    # Brute force: whenever the fit step moved the tile, no smaller tile at
+    # or above the first estimate fits, and the chosen one does (or gives
+    # S_b = 1 everywhere).
+    import random
+    rnd = random.Random(7)
+    for _ in range(400):
+        batch = rnd.choice([1, 2, 3, 5, 8])
+        heads = rnd.choice([16, 64, 128])
+        ctx = [rnd.choice([0, 33, 4096, 20000, 32768, 81920, 131072, rnd.randint(0, 131072)])
+               for _ in range(batch)]
+        cus = rnd.choice([8, 64, 256, 304])
+        r = plan.choose_partitions(batch, heads, 1, ctx, plan.PlanParams(num_cus=cus))
+        nblk = [-(-n // 32) for n in ctx]
+        G = r["groups"]
+        first = max(4, -(-G * sum(nblk) // cus))
+
+        def wgs(t):
+            return G * sum(p * max(1, -(-(-(-nb // p)) // t)) for nb, p in zip(nblk, r["P"]))
+        t = r["tile_blocks"]
+        assert t >= first
+        if t > first:
+            assert all(wgs(u) > cus for u in range(first, t))
+            assert wgs(t) <= cus or all(s == 1 for s in r["S"])
+        assert r["S"] == [max(1, -(-(-(-nb // p)) // t)) for nb, p in zip(nblk, r["P"])]
