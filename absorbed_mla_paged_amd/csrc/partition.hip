@@ -425,7 +425,7 @@ extern "C" int mla_decode_partition(
   if (dtype != MLA_F16 && dtype != MLA_BF16) return fail(MLA_E_UNSUPPORTED, "dtype %d", dtype);
   const int32_t hpw = heads_per_wg ? heads_per_wg : default_heads_per_wg(num_heads);
   if (!valid_heads_per_wg(num_heads, hpw))
-    return fail(MLA_E_UNSUPPORTED, "heads_per_wg %d for %d heads (16, 64 or 128 dividing it)",
+    return fail(MLA_E_UNSUPPORTED, "heads_per_wg %d for %d heads (16 or 64 dividing it)",
                 hpw, num_heads);
   if (!std::isfinite(scale)) return fail(MLA_E_RANGE, "scale is not finite");
   if (batch == 0) return MLA_OK;

@@ -123,8 +123,8 @@ __device__ __forceinline__ void bump_counter(MLA_LDS uint32_t* c, int lane) {
 }
 #endif  // __HIPCC__
 
-// Launch of the wide kernel (heads_per_wg 64 or 128); arguments as the
-// 16-head kernel's. Host side, after the launcher's checks.
+// Launch of the wide kernel (heads_per_wg 64); arguments as the 16-head
+// kernel's. Host side, after the launcher's checks.
 void launch_wide(int dtype, int hpw, unsigned wgs, hipStream_t stream, int32_t groups,
                  int32_t rows_per_req, int32_t slots, int32_t direct, int32_t total_rows,
                  int32_t max_blocks, const int32_t* context_lens, const int32_t* row_indptr,

@@ -49,7 +49,7 @@ int default_heads_per_wg(int32_t heads) {
 }
 
 bool valid_heads_per_wg(int32_t heads, int32_t hpw) {
-  return (hpw == 16 || hpw == 64 || hpw == 128) && heads % hpw == 0;
+  return (hpw == 16 || hpw == 64) && heads % hpw == 0;
 }
 
 TileRange tile_range(int64_t n, int32_t P, int32_t S, int32_t p, int32_t s) {

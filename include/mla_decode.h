@@ -81,9 +81,9 @@ typedef struct {
   int32_t min_partitions;        /* lower clamp of the policy count (2) */
   int32_t max_partitions;        /* upper clamp, <= MLA_MAX_PARTITIONS (8) */
   int32_t num_cus;               /* compute units; 0 = ask the current device */
-  int32_t heads_per_wg;          /* heads per workgroup: 16, 64 or 128 dividing
-                                    H; 0 = library default (64 if 64 divides
-                                    H, else 16) */
+  int32_t heads_per_wg;          /* heads per workgroup: 16 or 64, dividing H;
+                                    0 = library default (64 if 64 divides H,
+                                    else 16) */
   int32_t min_tile_blocks;       /* smallest device tile in 32-token blocks (4) */
   int32_t wgs_per_cu;            /* device tiling target: workgroups per CU (1) */
   int32_t force_partitions;      /* >0: every request gets P_b = this */

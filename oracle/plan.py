@@ -123,7 +123,7 @@ def choose_partitions(batch: int, heads: int, q_len: int, ctx, params: PlanParam
     if prm.workspace_limit_bytes < 0:
         raise ValueError("limit")
     hpw = prm.heads_per_wg or default_heads_per_wg(heads)
-    if hpw not in (16, 64, 128) or heads % hpw:
+    if hpw not in (16, 64) or heads % hpw:
         raise ValueError("heads per workgroup")
     G = heads // hpw
     nblk = [_cdiv(n, block_size) for n in ctx]

@@ -186,6 +186,8 @@ def test_decode_partition_host_checks_launch_nothing():
     assert call(heads=160) == -6
     assert call(dtype=7) == -6
     assert call(hpw=32) == -6
+    assert call(heads=128, hpw=128) == -6   # no 128-head layout
+    assert call(heads=96, hpw=64) == -6     # 64 must divide H
     assert call(scale=float("nan")) == -3
     assert call(qa=None) == -1
     assert call(po=None) == -1          # split plan without workspace

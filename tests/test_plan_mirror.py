@@ -77,22 +77,22 @@ def test_workspace_shedding_order():
     heads = 128
     ctx = [131072, 4096, 40000, 90000]
     row = heads * 513 * 4
-    free = plan.choose_partitions(4, heads, 1, ctx, plan.PlanParams(heads_per_wg=128))
+    free = plan.choose_partitions(4, heads, 1, ctx, plan.PlanParams(heads_per_wg=64))
     assert free["workspace_bytes"] == free["total_rows"] * row
     # Step 1: tiles grow until S is 1 everywhere.
     lim = sum(free["P"]) * row
     r = plan.choose_partitions(4, heads, 1, ctx,
-                               plan.PlanParams(heads_per_wg=128, workspace_limit_bytes=lim))
+                               plan.PlanParams(heads_per_wg=64, workspace_limit_bytes=lim))
     assert r["S"] == [1, 1, 1, 1] and r["P"] == free["P"]
     # Step 2: the largest P comes down first, not below 2.
     lim2 = (sum(free["P"]) - 3) * row
     r = plan.choose_partitions(4, heads, 1, ctx,
-                               plan.PlanParams(heads_per_wg=128, workspace_limit_bytes=lim2))
+                               plan.PlanParams(heads_per_wg=64, workspace_limit_bytes=lim2))
     assert sum(r["P"]) == sum(free["P"]) - 3 and min(p for p in r["P"]) >= 1
     assert r["workspace_bytes"] <= lim2
     # Step 3: down to single pass, which needs no workspace at all.
     r = plan.choose_partitions(4, heads, 1, ctx,
-                               plan.PlanParams(heads_per_wg=128, workspace_limit_bytes=1))
+                               plan.PlanParams(heads_per_wg=64, workspace_limit_bytes=1))
     assert r["P"] == [1] * 4 and r["S"] == [1] * 4 and r["workspace_bytes"] == 0
 
 
