@@ -30,6 +30,30 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 KV_BYTES_PER_TOKEN = (512 + 64) * 2
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "absorbed_mla_paged_amd", "csrc")
+# Sources of each partition kernel; their hash keys the counter table below.
+KERNEL_SOURCES = {
+    16: ["partition.hip", "partition_common.h", "device_common.h"],
+    64: ["partition_wide.hip", "partition_common.h", "device_common.h"],
+}
+# HBM traffic per partition launch from rocprofv3 --pmc (FETCH_SIZE and
+# WRITE_SIZE in KiB per dispatch, separate runs), keyed by workload and the
+# kernel source hash at the time of measurement; the summaries are in
+# profiles/. FETCH_SIZE on this part reads half of what a plain copy of known
+# size moves, WRITE_SIZE reads exactly it: the scale factors below.
+FETCH_SCALE = 2.0
+WRITE_SCALE = 1.0
+MEASURED = {}
+
+
+def kernel_hash(hpw: int) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[hpw]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:12]
 
 
 def log(*a):
@@ -55,7 +79,7 @@ def cpu_baseline(case, budget_s: float):
     t0 = time.perf_counter()
     oracle.latent_f64(case)
     one = time.perf_counter() - t0
-    reps = max(1, min(50, int(budget_s / max(one, 1e-3))))
+    reps = max(1, min(5000, int(budget_s / max(one, 1e-3))))
     t0 = time.perf_counter()
     for _ in range(reps):
         oracle.latent_f64(case)
@@ -74,7 +98,7 @@ def main():
     ap.add_argument("--single-pass", action="store_true", help="force P = S = 1")
     ap.add_argument("--cold-bytes", type=float, default=1.5e9,
                     help="bytes of distinct KV copies cycled through (MALL is 256 MB)")
-    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=100)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -195,6 +219,13 @@ def main():
     achieved = alg["partition"] / (part_us * 1e-6) / 1e9
     split_bytes = info["total_rows"] * case.heads * 513 * 4 if info["needs_reduce"] else 0
     pair_gbs = alg["total"] / (ms_per_step * 1e-3) / 1e9
+    khash = kernel_hash(info["heads_per_wg"])
+    meas = MEASURED.get((args.workload, khash))
+    traffic = None
+    if meas is not None:
+        traffic = int(round((meas["fetch_kib"] * FETCH_SCALE + meas["write_kib"] * WRITE_SCALE) * 1024))
+    log(f"[bench] partition kernel source hash {khash}; counters "
+        f"{'on record' if meas else 'not on record for this source'}")
     log(f"[bench] partition kernel {part_us:.2f} us -> {achieved:.0f} GB/s "
         f"({100 * achieved / HBM_PEAK_GBS:.1f}% of 8 TB/s); pair {pair_gbs:.0f} GB/s; "
         f"split overhead {split_bytes / 1e6:.2f} MB written")
@@ -225,9 +256,12 @@ def main():
         "achieved_gbs_pair": round(pair_gbs, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "partition_kernel",
+                     "traffic": traffic,
+                     "kernel": "partition_kernel" if info["heads_per_wg"] == 16 else "wide_kernel",
+                     "kernel_source_hash": khash,
                      "kernel_us": round(part_us, 3),
-                     "algorithmic_bytes": alg["partition"]},
+                     "algorithmic_bytes": alg["partition"],
+                     "mfma_busy": meas.get("mfma_busy") if meas else None},
         "cpu_baseline": cpu,
         "host": platform.node(),
     }
