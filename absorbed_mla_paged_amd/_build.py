@@ -16,6 +16,9 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla_decode.so")
 SOURCES = ["plan.cpp", "partition.hip", "partition_wide.hip", "reduce.hip"]
 HEADERS = ["internal.h", "device_common.h", "partition_common.h"]
+# Per-source extra flags. The 64-head kernel runs two waves per SIMD (256
+# registers each) and keeps its MFMA accumulators in VGPRs.
+EXTRA = {"partition_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:
@@ -24,25 +27,42 @@ def hipcc() -> str:
     return cand if os.path.exists(cand) else "hipcc"
 
 
-def command(out: str = LIB, extra=()) -> list[str]:
-    return [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-            "-Wall", "-Wno-unused-function",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-mllvm", "-amdgpu-kernarg-preload-count=16",
-            "-I", os.path.join(HERE, "..", "include"),
-            *extra, "-o", out, *[os.path.join(CSRC, s) for s in SOURCES]]
+COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+          "-Wall", "-Wno-unused-function",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-kernarg-preload-count=16"]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+def compile_command(src: str, obj: str) -> list[str]:
+    return [hipcc(), *COMMON, *EXTRA.get(src, []), "-I", os.path.join(HERE, "..", "include"),
+            "-c", os.path.join(CSRC, src), "-o", obj]
+
+
+def link_command(objs, out: str) -> list[str]:
+    return [hipcc(), "--offload-arch=gfx950", "-fPIC", "-shared", *objs, "-o", out]
+
+
+def _run(cmd, verbose):
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "packed-fp32-ops' is not a recognized feature"
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
     if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+        raise RuntimeError(f"{' '.join(cmd[:3])} ... failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+    with tempfile.TemporaryDirectory(prefix="mla_build_") as tmpd:
+        objs = [os.path.join(tmpd, s + ".o") for s in SOURCES]
+        with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+            for f in [ex.submit(_run, compile_command(s, o), verbose)
+                      for s, o in zip(SOURCES, objs)]:
+                f.result()
+        tmp = LIB + ".tmp"
+        _run(link_command(objs, tmp), verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -5,43 +5,43 @@
 // Same computation as the 16-head kernel (mlxcel pull request 995, "What
 // changed", Stage 1; vllm-metal pull request 601 "[kernel] Wire MLA
 // split-KV decode", "What changed"): for one row (a block-aligned token
-// range of one request) and a group of heads, the base-2 online softmax over
+// range of one request) and a group of heads, the base-2 softmax over
 //   s_t = scale * (q_absorbed . ckv_t + q_pe . kpe_t)
 // applied to the 512-wide ckv rows, written as a normalised fp32 partial and
 // its log2-sum-exp, or rounded into `out` for a single-row request.
 //
-// With 64 heads the work per cached token is dense enough for the matrix
-// cores to matter, so each LDS fragment should feed as many heads as the
-// registers allow:
-//  * 256 threads = 4 wave64, one per SIMD. Waves 2p and 2p+1 form pair p,
-//    which owns heads 32p .. 32p+31 of the workgroup; wave 2p+h owns head
-//    tile h of the pair (16 heads), whose Q (16 x 576, the score B operand)
-//    sits in 72 VGPRs.
-//  * Scores: each wave scores all 32 tokens of the block for its 16 heads,
-//    S^T[token, head] = K[token, :] . Q^T[:, head] on v_mfma_f32_16x16x32
-//    (2 token tiles x 18 K-steps), and runs the softmax of those heads.
-//    The pair then swaps its 16-bit probabilities through LDS.
-//  * Values: wave 2p+h accumulates O^T[dim, head] for dims 256h .. 256h+255
-//    and both head tiles of the pair (128 registers) on v_mfma_f32_16x16x32;
-//    the MFMA result layout of S^T is already the B-operand layout of P^T,
-//    and V^T comes from the same LDS tile through ds_read_b64_tr_b16, each
-//    fragment feeding both head tiles. The running sums are swapped once,
-//    at the end.
-//  * LDS holds a ring of 4 one-block slots (32 KB ckv + 4 KB kpe each);
-//    block k lives in slot k % 4, so three blocks are in flight while one is
-//    used. Every wave copies a quarter of each block with
-//    global_load_lds_dwordx4 (16 B per lane) and waits only for its own
-//    copies; one s_barrier per block then makes the block visible to all and
-//    also proves that every wave is done with the previous block, whose slot
-//    is refilled right away with block k + 3. A second s_barrier per block
-//    publishes the swapped probabilities.
-//  * No rescaling inside the loop: every head's reference maximum is fixed
-//    by the first block, and probabilities relative to it may grow up to
-//    2^15 (finite in fp16 and bf16, exact to the format's precision). The
-//    true running maximum is tracked alongside; if it ends more than 15
-//    (base 2) above the reference for any head, the workgroup makes a
-//    second pass over the row with the exact maximum as reference. The
-//    accumulators thus only ever see MFMA updates and stay in AGPRs.
+// With 64 heads the arithmetic per cached byte is high enough that the
+// matrix cores and LDS, not HBM, set the pace, so the layout keeps each
+// SIMD's MFMA pipe fed from two waves with different jobs:
+//  * 512 threads = 8 wave64, two per SIMD (256 registers each; the MFMA
+//    accumulators live in VGPRs). Waves 0-3 score, waves 4-7 apply values.
+//  * Score wave s scores tokens 16 (s / 2) .. +16 of a 32-token block for
+//    heads 32 (s % 2) .. +32 of the workgroup, S^T[token, head] =
+//    K[token, :] . Q^T[:, head] on v_mfma_f32_16x16x32 (18 K-steps); Q of
+//    its 32 heads (the B operand) sits in 144 VGPRs, so each K fragment read
+//    from LDS feeds two MFMAs. It then turns its scores into 16-bit
+//    probabilities and publishes them in LDS.
+//  * Value wave v accumulates O^T[dim, head] for dims 128 v .. +128 and all
+//    64 heads (128 VGPRs) on v_mfma_f32_16x16x32. The MFMA result layout of
+//    S^T is already the B-operand layout of P^T; V^T is read from the same
+//    LDS tile with ds_read_b64_tr_b16, each fragment feeding four MFMAs.
+//  * Pipeline: in step i the score waves work on block i while the value
+//    waves apply block i - 1 (probabilities double-buffered by parity); one
+//    s_barrier per step. LDS holds a ring of 4 one-block slots (32 KB ckv +
+//    4 KB kpe); the value waves copy blocks in with global_load_lds_dwordx4
+//    (16 B per lane, a quarter of each block per wave), one copy between
+//    the MFMAs of each value fragment: a copy can hold its wave at issue for
+//    its share of the CU's vector-memory rate, and meanwhile the score wave
+//    on the same SIMD keeps the MFMA pipe busy.
+//  * No rescaling inside the loop: every head's reference maximum is the
+//    maximum over the row's first block, and probabilities relative to it
+//    may grow up to 2^15 (finite in fp16 and bf16, exact to the format's
+//    precision). Each score lane tracks the true maximum of its own scores;
+//    if any ends more than 15 (base 2) above its head's reference, the
+//    workgroup makes a second pass over the row with the exact maxima as
+//    references. The accumulators only ever see MFMA updates.
+//  * LDS fragment reads in the MFMA loops are issued several MFMAs ahead
+//    (dev::lds_read_*), with explicit lgkmcnt waits.
 #include "partition_common.h"
 
 #include <cmath>
@@ -56,18 +56,21 @@ constexpr int HPW = 64;                         // heads per workgroup
 constexpr int SLOT = BS * (CKV_ROW + KPE_ROW);  // 36 KB per one-block slot
 constexpr int SLOT_KPE = BS * CKV_ROW;          // kpe rows after the ckv rows
 constexpr int NSLOT = 4;
-constexpr int WAVES = 4;
+constexpr int WAVES = 8;
 constexpr int THREADS = 64 * WAVES;
-constexpr int DT_WAVE = LAT / 16 / 2;           // 16 output dim tiles per wave
+constexpr int NSC = 4;                          // score waves (0..3)
+constexpr int DT_WAVE = LAT / 16 / 4;           // 8 output dim tiles per value wave
+constexpr int HT_ALL = HPW / 16;                // 4 head tiles per workgroup
 constexpr int OPS = BS + BS * KPE_ROW / 1024;   // 36 copy instructions per block
-constexpr int OPW = OPS / WAVES;                // 9 per wave
-constexpr int XP = NSLOT * SLOT;                // swapped probabilities [wave][lane]
-constexpr int XML = XP + WAVES * 64 * 16;       // swapped (max, sum) [wave][16 heads]
-constexpr int XFLAG = XML + WAVES * 16 * 8;     // "second pass needed" flag
+constexpr int OPW = OPS / 4;                    // 9 per value wave
+constexpr int XP = NSLOT * SLOT;                // probabilities [parity][wave][lane] 16 B
+constexpr int XM = XP + 2 * NSC * 64 * 16;      // per-head floats [wave][2][16]
+constexpr int XFLAG = XM + NSC * 32 * 4;        // "second pass needed" flag
 constexpr int LDS_BYTES = XFLAG + 16;
 constexpr float HEADROOM_LOG2 = 15.0f;          // p <= 2^15 against the reference
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-static_assert(OPS % WAVES == 0 && 3 * OPW < 64, "copy split / vmcnt range");
+static_assert(OPS % 4 == 0 && 3 * OPW < 64, "copy split / vmcnt range");
+static_assert(OPW == DT_WAVE + 1, "one copy per value fragment, plus one");
 
 // Wait until at most `later` blocks' worth of this wave's copies are still
 // in flight (copies complete in issue order).
@@ -107,24 +110,14 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 15;   // MFMA row/column inside a 16-wide tile
   const int lg = lane >> 4;   // MFMA k-group (0..3)
-  const int half = wave & 1;  // my head tile of the pair; my dim half
+  const bool scorer = wave < NSC;
+  const int sw = wave & 3;    // index within the role
+  const int hp = sw & 1;      // score waves: my 32 heads are 32 hp .. +32
+  const int tt = sw >> 1;     // score waves: my 16 tokens are 16 tt .. +16
 
   int b, x, hg;
   if (!slot_of(blockIdx.x, groups, rows_per_req, slots, &b, &x, &hg)) return;
-  const int head0 = hg * HPW + (wave >> 1) * 32;   // this pair's first head
-  const int64_t qrow0 = (int64_t)b * a.heads + head0;
-
-  // Q first (its address needs no metadata): lane (ln, lg) holds head
-  // head0 + 16 half + ln, dims 32 k + 8 lg .. + 8.
-  vec8 q[KSTEPS];
-  {
-    const int64_t qr = qrow0 + 16 * half + ln;
-    const vec8* qa = reinterpret_cast<const vec8*>(a.q_absorbed + qr * LAT);
-    const vec8* qp = reinterpret_cast<const vec8*>(a.q_pe + qr * ROPE);
-#pragma unroll
-    for (int k = 0; k < KSTEPS; ++k)
-      q[k] = (k < LAT / 32) ? qa[4 * k + lg] : qp[4 * (k - LAT / 32) + lg];
-  }
+  const int hwg = hg * HPW;   // first head of the workgroup
 
   RowInfo ri;
   if (!find_row(b, x, direct, total_rows, max_blocks, context_lens, row_indptr, partitions,
@@ -132,23 +125,23 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
     return;
   const int row = ri.row;
   const int nblocks = ri.nblocks;
-  // Lane (ln, lg) of head tile ht and dim tile dt holds head head0 + 16 ht +
-  // ln, dims 16 dt + 4 lg .. + 4.
+  // Output of value-wave lane (ln, lg) for head tile ht (head hwg + 16 ht +
+  // ln) and dim tile dt (dims 16 dt + 4 lg .. + 4).
   auto store = [&](int ht, int dt, f32x4 v) {
-    const int64_t h = head0 + 16 * ht + ln;
+    const int64_t h = hwg + 16 * ht + ln;
     const int d0 = dt * 16 + lg * 4;
     if (direct) {
       vec4 hv;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) hv[j] = static_cast<scalar>(v[j]);
+      for (int e = 0; e < 4; ++e) hv[e] = static_cast<scalar>(v[e]);
       *reinterpret_cast<vec4*>(reinterpret_cast<uint16_t*>(a.out) +
                                ((int64_t)b * a.heads + h) * LAT + d0) = hv;
     } else {
       *reinterpret_cast<f32x4*>(a.partial_out + ((int64_t)row * a.heads + h) * LAT + d0) = v;
     }
   };
-  auto store_lse = [&](int ht, float v) {
-    const int64_t i = (int64_t)(direct ? b : row) * a.heads + head0 + 16 * ht + ln;
+  auto store_lse = [&](int h_local, float v) {
+    const int64_t i = (int64_t)(direct ? b : row) * a.heads + hwg + h_local;
     if (direct) {
       if (a.lse2_out) a.lse2_out[i] = v;
     } else {
@@ -161,12 +154,13 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
   }
 
   if (nblocks <= 0) {
-    // No visible token: zero output, lse2 = -inf.
+    // No visible token: zero output, lse2 = -inf (value waves write it).
+    if (scorer) return;
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
+    for (int ht = 0; ht < HT_ALL; ++ht) {
 #pragma unroll
-      for (int d = 0; d < DT_WAVE; ++d) store(ht, half * DT_WAVE + d, f32x4{0.f, 0.f, 0.f, 0.f});
-      if (half == 0 && lg == 0) store_lse(ht, -INFINITY);
+      for (int d = 0; d < DT_WAVE; ++d) store(ht, sw * DT_WAVE + d, f32x4{0.f, 0.f, 0.f, 0.f});
+      if (sw == 0 && lg == 0) store_lse(16 * ht + ln, -INFINITY);
     }
     return;
   }
@@ -180,208 +174,280 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
     const int v = __builtin_amdgcn_readfirstlane(load_const(block_table, tbl0 + k));
     return (int64_t)max(0, min(v, last_phys));
   };
-  // This wave's quarter of block k's copies into slot k % 4: ops 0..31 are
-  // ckv rows, 32..35 kpe rows 8 (op - 32) .. + 8. Chunk c of an LDS row sits
-  // at position c ^ swizzle(row).
-  auto issue = [&](int k, int64_t phys) {
+  // Value wave sw's quarter of block k's copies into slot k % 4: copy i is
+  // op 9 sw + i; ops 0..31 are ckv rows, 32..35 kpe rows 8 (op - 32) .. + 8.
+  // Chunk c of an LDS row sits at position c ^ swizzle(row).
+  auto issue_one = [&](int k, int64_t phys, int i) {
     const uint32_t base = lds0 + (k & (NSLOT - 1)) * SLOT;
-#pragma unroll
-    for (int i = 0; i < OPW; ++i) {
-      const int op = wave * OPW + i;
-      if (op < BS) {
-        const uint32_t voff = ((lane & ~15) | ((lane & 15) ^ swz_ckv(op))) * 16;
-        dma16s(voff, ckv_base + phys * (BS * CKV_ROW) + op * CKV_ROW, base + op * CKV_ROW);
-      } else {
-        const int t8 = op - BS;
-        const int r = t8 * 8 + (lane >> 3);
-        const uint32_t voff = (lane >> 3) * KPE_ROW + ((lane & 7) ^ swz_kpe(r)) * 16;
-        dma16s(voff, kpe_base + phys * (BS * KPE_ROW) + t8 * 1024, base + SLOT_KPE + t8 * 1024);
-      }
+    const int op = sw * OPW + i;
+    if (op < BS) {
+      const uint32_t voff = ((lane & ~15) | ((lane & 15) ^ swz_ckv(op))) * 16;
+      dma16s(voff, ckv_base + phys * (BS * CKV_ROW) + op * CKV_ROW, base + op * CKV_ROW);
+    } else {
+      const int t8 = op - BS;
+      const int r = t8 * 8 + (lane >> 3);
+      const uint32_t voff = (lane >> 3) * KPE_ROW + ((lane & 7) ^ swz_kpe(r)) * 16;
+      dma16s(voff, kpe_base + phys * (BS * KPE_ROW) + t8 * 1024, base + SLOT_KPE + t8 * 1024);
     }
   };
 
-  // Loop-invariant LDS byte offsets inside a slot. Score fragments of
-  // token tile tt: row 16 tt + ln (tile 1 is 16 KB further, same swizzle),
-  // chunk 4 k + lg; chunks 16 apart keep the same swizzled low bits, so
-  // k = 4 m + kk is offs_k[kk] + 256 m. Value fragments: rows r1 = 4 lg +
-  // ln / 4 and r1 + 16 (16 KB further), chunk 2 dt + (ln / 2) % 2; dt =
-  // 8 m + dd is offs_v[dd] + 256 m.
-  uint32_t offs_k[4], offs_p[2], offs_v[8];
+  // Loop-invariant LDS byte offsets inside a slot. Score fragment (K-step
+  // ks): row 16 tt + ln, chunk 4 ks + lg; chunks 16 apart keep the same
+  // swizzled low bits, so ks = 4 m + kk is offs_k[kk] + 256 m. Value
+  // fragment d: dim tile 8 sw + d, rows r1 = 4 lg + ln / 4 and r1 + 16
+  // (16 KB further, same swizzle), chunk 2 (8 sw + d) + (ln / 2) % 2.
+  const int rk = 16 * tt + ln;
+  uint32_t offs_k[4], offs_p[2], offs_v[DT_WAVE];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) offs_k[kk] = ln * CKV_ROW + (((4 * kk + lg) ^ swz_ckv(ln)) * 16);
+  for (int kk = 0; kk < 4; ++kk) offs_k[kk] = rk * CKV_ROW + (((4 * kk + lg) ^ swz_ckv(rk)) * 16);
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
-    offs_p[kk] = SLOT_KPE + ln * KPE_ROW + (((4 * kk + lg) ^ swz_kpe(ln)) * 16);
+    offs_p[kk] = SLOT_KPE + rk * KPE_ROW + (((4 * kk + lg) ^ swz_kpe(rk)) * 16);
   const int r1 = 4 * lg + (ln >> 2);
 #pragma unroll
-  for (int dd = 0; dd < 8; ++dd)
-    offs_v[dd] = r1 * CKV_ROW + (((2 * dd + ((ln >> 1) & 1)) ^ swz_ckv(r1)) * 16) + (ln & 1) * 8;
-  MLA_LDS char* xp_mine = smem + XP + wave * 1024;
-  const MLA_LDS char* xp_pair = smem + XP + (wave ^ 1) * 1024;
+  for (int d = 0; d < DT_WAVE; ++d)
+    offs_v[d] = r1 * CKV_ROW + ((((2 * d + ((ln >> 1) & 1)) ^ swz_ckv(r1)) + 16 * sw) * 16) +
+                (ln & 1) * 8;
+  MLA_LDS float* xm = (MLA_LDS float*)(smem + XM);   // [score wave][j][ln]
   MLA_LDS uint32_t* flag = (MLA_LDS uint32_t*)(smem + XFLAG);
   if (tid == 0) *flag = 0u;   // seen by all after the first meeting below
 
   const float c2 = a.scale_log2;
   const int ntok = ri.tok_hi - ri.tok_lo;
-  f32x4 o[DT_WAVE][2];
-  float m_ref = -INFINITY;   // reference max of my head (base 2)
-  float m_run = -INFINITY;   // true running max of my head
-  float l_part = 0.f;        // this lane's share of my head's sum
 
-  // Q must be in registers before any copy is issued: the copies are
-  // invisible to the compiler's own wait counting.
-  wait_vmcnt<0>();
-  for (int pass = 0; pass < 2; ++pass) {
-    if (pass == 1) m_ref = m_run;   // exact maximum: every p <= 1
+  // The two roles run separate copies of the pass / step loops (so Q and
+  // the accumulators are never live in the same wave) that meet at the same
+  // barriers in the same order:
+  //   per step i:      M_step(i)  [+ M_ref in step 0 of the first pass]
+  //   after a pass:    M_flag     [+ M_x1, M_x2 before a second pass]
+  //   epilogue:        M_epi
+  if (scorer) {
+    // Q: lane (ln, lg) of head tile j holds head hwg + 32 hp + 16 j + ln,
+    // dims 32 k + 8 lg .. + 8. Score waves issue no copies, so the
+    // compiler's own wait for these loads is exact; the first block takes
+    // longer to arrive than Q.
+    vec8 q[2][KSTEPS];
 #pragma unroll
-    for (int d = 0; d < DT_WAVE; ++d) o[d][0] = o[d][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    l_part = 0.f;
-    for (int k = 0; k < NSLOT && k < nblocks; ++k) issue(k, phys_of(k));
+    for (int j = 0; j < 2; ++j) {
+      const int64_t qr = (int64_t)b * a.heads + hwg + 32 * hp + 16 * j + ln;
+      const vec8* qa = reinterpret_cast<const vec8*>(a.q_absorbed + qr * LAT);
+      const vec8* qp = reinterpret_cast<const vec8*>(a.q_pe + qr * ROPE);
+#pragma unroll
+      for (int k = 0; k < KSTEPS; ++k)
+        q[j][k] = (k < LAT / 32) ? qa[4 * k + lg] : qp[4 * (k - LAT / 32) + lg];
+    }
+    float m_ref[2] = {-INFINITY, -INFINITY};  // reference maxima of my heads
+    float m_run[2] = {-INFINITY, -INFINITY};  // max of this lane's own scores
+    float l_part[2] = {0.f, 0.f};             // this lane's share of the sums
+    for (int pass = 0; pass < 2; ++pass) {
+      l_part[0] = l_part[1] = 0.f;
+      for (int i = 0; i <= nblocks; ++i) {
+        meet();   // M_step(i): block i is in LDS; P(i - 2)'s buffer is free
+        if (i >= nblocks) continue;
+        // ---- scores: my 16 tokens x 32 heads of block i -----------------------
+        const uint32_t sbase = lds0 + (i & (NSLOT - 1)) * SLOT;
+        const int valid = min(BS, ntok - i * BS);
+        auto kaddr = [&](int ks) {
+          return sbase + ((ks < LAT / 32) ? offs_k[ks & 3] + 256 * (ks >> 2)
+                                          : offs_p[ks - LAT / 32]);
+        };
+        constexpr int KD = 5;
+        f32x4 acc[2][2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        vec8 kf[KSTEPS];
+#pragma unroll
+        for (int ks = 0; ks < KD; ++ks) kf[ks] = lds_read_b128<vec8>(kaddr(ks));
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          if (ks + KD <= KSTEPS) lds_wait<KD - 1>(kf[ks]);
+          else lds_wait<0>(kf[ks]);   // tail: fewer than KD - 1 reads after ks
+          acc[0][ks & 1] = E::mfma(kf[ks], q[0][ks], acc[0][ks & 1]);
+          acc[1][ks & 1] = E::mfma(kf[ks], q[1][ks], acc[1][ks & 1]);
+          if (ks + KD < KSTEPS) kf[ks + KD] = lds_read_b128<vec8>(kaddr(ks + KD));
+        }
+        // Lane (ln, lg) holds head 32 hp + 16 j + ln at tokens 16 tt + 4 lg + e.
+        float sc[2][4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const f32x4 sv = acc[j][0] + acc[j][1];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sc[j][e] = (16 * tt + 4 * lg + e < valid) ? sv[e] * c2 : -INFINITY;
+            m_run[j] = fmaxf(m_run[j], sc[j][e]);
+          }
+        }
+        if (pass == 0 && i == 0) {
+          // Reference maxima over the whole first block: both token halves
+          // (score waves s and s ^ 2 hold the same heads).
+          float bm[2];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            bm[j] = fmaxf(fmaxf(sc[j][0], sc[j][1]), fmaxf(sc[j][2], sc[j][3]));
+            bm[j] = fmaxf(bm[j], shfl_xor(bm[j], 16));
+            bm[j] = fmaxf(bm[j], shfl_xor(bm[j], 32));
+            if (lg == 0) xm[(sw * 2 + j) * 16 + ln] = bm[j];
+          }
+          meet();   // M_ref
+#pragma unroll
+          for (int j = 0; j < 2; ++j) m_ref[j] = fmaxf(bm[j], xm[((sw ^ 2) * 2 + j) * 16 + ln]);
+        }
+        u32x4 pme;   // 16-bit P: head tile 0 tokens e = 0..3, then head tile 1
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          scalar p[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            p[e] = static_cast<scalar>(__builtin_amdgcn_exp2f(sc[j][e] - m_ref[j]));
+            l_part[j] += static_cast<float>(p[e]);
+          }
+          pme[2 * j] = (uint32_t)__builtin_bit_cast(uint16_t, p[0]) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, p[1]) << 16);
+          pme[2 * j + 1] = (uint32_t)__builtin_bit_cast(uint16_t, p[2]) |
+                           ((uint32_t)__builtin_bit_cast(uint16_t, p[3]) << 16);
+        }
+        *(MLA_LDS u32x4*)(smem + XP + (((i & 1) * NSC + sw) * 64 + lane) * 16) = pme;
+      }
+      if (pass == 1) break;
+      // Did any score outgrow its head's reference?
+      if (__any(m_run[0] > m_ref[0] + HEADROOM_LOG2 || m_run[1] > m_ref[1] + HEADROOM_LOG2) &&
+          lane == 0)
+        *flag = 1u;
+      meet();   // M_flag
+      if (*(const volatile MLA_LDS uint32_t*)flag == 0u) break;
+      // Second pass: references become the exact maxima of the row.
+      float mr[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        mr[j] = fmaxf(m_run[j], shfl_xor(m_run[j], 16));
+        mr[j] = fmaxf(mr[j], shfl_xor(mr[j], 32));
+        if (lg == 0) xm[(sw * 2 + j) * 16 + ln] = mr[j];
+      }
+      meet();   // M_x1
+#pragma unroll
+      for (int j = 0; j < 2; ++j) m_ref[j] = fmaxf(mr[j], xm[((sw ^ 2) * 2 + j) * 16 + ln]);
+      meet();   // M_x2: xm is free again
+    }
+    // ---- epilogue: publish my heads' sums; write the LSE -------------------
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float lt = l_part[j] + shfl_xor(l_part[j], 16);
+      lt += shfl_xor(lt, 32);
+      if (lg == 0) xm[(sw * 2 + j) * 16 + ln] = lt;
+    }
+    meet();   // M_epi
+    if (tt == 0 && lg == 0) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float l = xm[(sw * 2 + j) * 16 + ln] + xm[((sw + 2) * 2 + j) * 16 + ln];
+        store_lse(32 * hp + 16 * j + ln, m_ref[j] + __builtin_amdgcn_logf(l));
+      }
+    }
+    return;
+  }
+
+  // ---- value waves ----------------------------------------------------------
+  // Their only vector-memory operations before the end are the copies
+  // (counted by wait_blocks); the debug store above is wave 0's.
+  f32x4 o[DT_WAVE][HT_ALL];
+  for (int pass = 0; pass < 2; ++pass) {
+    // An opaque zero: a literal one would be hoisted out of the pass loop
+    // and kept alive next to the accumulators.
+    float zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+#pragma unroll
+    for (int d = 0; d < DT_WAVE; ++d)
+#pragma unroll
+      for (int ht = 0; ht < HT_ALL; ++ht) o[d][ht] = f32x4{zero, zero, zero, zero};
+    for (int k = 0; k < NSLOT && k < nblocks; ++k) {
+      const int64_t ph = phys_of(k);
+#pragma unroll
+      for (int c = 0; c < OPW; ++c) issue_one(k, ph, c);
+    }
     int64_t phys_next = nblocks > NSLOT ? phys_of(NSLOT) : 0;
 
-    for (int k = 0; k < nblocks; ++k) {
-      const int slot = k & (NSLOT - 1);
-      const int valid = min(BS, ntok - k * BS);
-
-      // This wave's copies of block k have landed: copies of blocks up to
-      // k + 2 (k + 3 for the first block) were issued before this point.
-      wait_blocks(min(k == 0 ? 3 : 2, nblocks - 1 - k));
-      if (valid < BS) {
-        // Rows past the context end may hold anything (NaN included): zero
-        // the ckv rows this wave brought in, so that 0-probability tokens
-        // add exactly 0.
-        for (int r = max(valid, wave * OPW); r < min(BS, (wave + 1) * OPW); ++r)
-          *(MLA_LDS u32x4*)(smem + slot * SLOT + r * CKV_ROW + lane * 16) = u32x4{0u, 0u, 0u, 0u};
-      }
-      meet();  // block k is in LDS; every wave is done with block k - 1
-      if (k >= 1 && k + NSLOT - 1 < nblocks) {
-        issue(k + NSLOT - 1, phys_next);   // into the slot of block k - 1
-        if (k + NSLOT < nblocks) phys_next = phys_of(k + NSLOT);
-      }
-
-      // ---- scores of my 16 heads over the 32 tokens ---------------------
-      // 36 K fragments (K-step ks, token tile tt) in the order j = 2 ks + tt,
-      // each read KD reads ahead of the MFMA that uses it; four
-      // accumulation chains.
-      const uint32_t sbase = lds0 + slot * SLOT;
-      auto kaddr = [&](int j) {
-        const int ks = j >> 1, tt = j & 1;
-        return sbase + ((ks < LAT / 32)
-                            ? offs_k[ks & 3] + 256 * (ks >> 2) + tt * (16 * CKV_ROW)
-                            : offs_p[ks - LAT / 32] + tt * (16 * KPE_ROW));
-      };
-      constexpr int NK = 2 * KSTEPS;
-      constexpr int KD = 6;
-      f32x4 acc[2][2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) acc[0][c] = acc[1][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-      vec8 kf[NK];
-#pragma unroll
-      for (int j = 0; j < KD; ++j) kf[j] = lds_read_b128<vec8>(kaddr(j));
-#pragma unroll
-      for (int j = 0; j < NK; ++j) {
-        if (j + KD <= NK) lds_wait<KD - 1>(kf[j]);
-        else lds_wait<0>(kf[j]);   // tail: reads after j are < KD - 1
-        const int ks = j >> 1, tt = j & 1;
-        acc[tt][ks & 1] = E::mfma(kf[j], q[ks], acc[tt][ks & 1]);
-        if (j + KD < NK) kf[j + KD] = lds_read_b128<vec8>(kaddr(j + KD));
-      }
-      // First value fragment now: its latency hides behind the softmax.
-      // Fragment d: dim tile 16 half + d, tokens 4 lg + (0..3) and
-      // 16 + 4 lg + (0..3) of the block.
-      auto vaddr = [&](int d) {
-        const int dt = half * DT_WAVE + d;
-        return sbase + offs_v[dt & 7] + 256 * (dt >> 3);
-      };
-      u32x2 vr[DT_WAVE][2];
-      vr[0][0] = lds_read_tr_b16(vaddr(0));
-      vr[0][1] = lds_read_tr_b16(vaddr(0) + 16 * CKV_ROW);
-
-      // ---- softmax weights of my heads (base 2) ----------------------------
-      // Lane (ln, lg) holds head 16 half + ln at tokens 16 tt + 4 lg + e.
-      float sc[2][4];
-      float bm = -INFINITY;
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const f32x4 sacc = acc[tt][0] + acc[tt][1];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sc[tt][e] = (16 * tt + 4 * lg + e < valid) ? sacc[e] * c2 : -INFINITY;
-          bm = fmaxf(bm, sc[tt][e]);
+    // Step i: apply block i - 1 (i >= 1) while the score waves score block i.
+    for (int i = 0; i <= nblocks; ++i) {
+      if (i < nblocks) {
+        // Block i must be in LDS when the step starts; copies of blocks up
+        // to min(max(3, i + 1), nblocks - 1) were issued before this point.
+        wait_blocks(min(max(NSLOT - 1, i + 1), nblocks - 1) - i);
+        const int valid = min(BS, ntok - i * BS);
+        if (valid < BS) {
+          // Rows past the context end may hold anything (NaN included): zero
+          // the ckv rows this wave brought in, so that 0-probability tokens
+          // add exactly 0.
+          for (int r = max(valid, sw * OPW); r < min(BS, (sw + 1) * OPW); ++r)
+            *(MLA_LDS u32x4*)(smem + (i & (NSLOT - 1)) * SLOT + r * CKV_ROW + lane * 16) =
+                u32x4{0u, 0u, 0u, 0u};
         }
       }
-      bm = fmaxf(bm, shfl_xor(bm, 16));
-      bm = fmaxf(bm, shfl_xor(bm, 32));
-      m_run = fmaxf(m_run, bm);
-      if (pass == 0 && k == 0) m_ref = bm;
-      // P^T B operand of lane (ln, lg): head 16 half + ln at tokens 4 lg + e
-      // (e < 4) and 16 + 4 lg + (e - 4) -- the order of the V^T reads.
-      vec8 pmine;
+      meet();                                   // M_step(i)
+      if (pass == 0 && i == 0) meet();          // M_ref
+      if (i < 1) continue;
+      // ---- values: block i - 1, dims 128 sw .. +128, all 64 heads -------------
+      const int kb = i - 1;
+      const uint32_t sbase = lds0 + (kb & (NSLOT - 1)) * SLOT;
+      // Refill the slot of block i - 2 (free since this step's meeting) with
+      // block i + 2, one copy per value fragment.
+      const bool refill = i >= 2 && i + 2 < nblocks;
+      const int64_t phys_fill = phys_next;
+      if (refill && i + 3 < nblocks) phys_next = phys_of(i + 3);
+      if (refill) issue_one(i + 2, phys_fill, 0);
+      // P^T B operand of head tile ht (pair ht / 2, tile ht % 2): tokens
+      // 4 lg + e from score wave ht / 2, 16 + 4 lg + e from score wave ht / 2 + 2.
+      const uint32_t pbase = lds0 + XP + ((kb & 1) * NSC * 64 + lane) * 16;
+      u32x4 pw[NSC];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const scalar p = static_cast<scalar>(__builtin_amdgcn_exp2f(sc[e >> 2][e & 3] - m_ref));
-        pmine[e] = p;
-        l_part += static_cast<float>(p);
-      }
-      // Swap with the pair partner (same lane, same layout).
-      *(MLA_LDS vec8*)(xp_mine + lane * 16) = pmine;
-      meet();   // also completes the first value fragment's reads
-      vec8 ppair = lds_read_b128<vec8>(lds_addr(xp_pair) + lane * 16);
-
-      // ---- values: my 256 dims, both head tiles -----------------------------
-      // Fragment d + VD is read while fragment d is used.
-      constexpr int VD = 3;
+      for (int v = 0; v < NSC; ++v) pw[v] = lds_read_b128<u32x4>(pbase + v * 64 * 16);
+      constexpr int VD = 3;   // value fragments read ahead
+      u32x2 vr[DT_WAVE][2];
 #pragma unroll
-      for (int d = 1; d <= VD; ++d) {
-        vr[d][0] = lds_read_tr_b16(vaddr(d));
-        vr[d][1] = lds_read_tr_b16(vaddr(d) + 16 * CKV_ROW);
+      for (int d = 0; d < VD; ++d) {
+        vr[d][0] = lds_read_tr_b16(sbase + offs_v[d]);
+        vr[d][1] = lds_read_tr_b16(sbase + offs_v[d] + 16 * CKV_ROW);
       }
-      lds_wait<2 * VD>(ppair);
-      const vec8 pv0 = half ? ppair : pmine;   // head tile 0 of the pair
-      const vec8 pv1 = half ? pmine : ppair;   // head tile 1
+      lds_wait<2 * VD>(pw[3]);
+      vec8 pv[HT_ALL];
+#pragma unroll
+      for (int ht = 0; ht < HT_ALL; ++ht) {
+        const u32x4 lo = pw[ht >> 1], hi = pw[(ht >> 1) + 2];
+        const int jj = 2 * (ht & 1);
+        pv[ht] = __builtin_bit_cast(vec8, u32x4{lo[jj], lo[jj + 1], hi[jj], hi[jj + 1]});
+      }
 #pragma unroll
       for (int d = 0; d < DT_WAVE; ++d) {
-        // Reads issued after fragment d: fragments d+1 .. min(d+VD, 15).
-        if (d > 0) {
-          if (d + VD < DT_WAVE) lds_wait<2 * VD>(vr[d][1]);
-          else if (d + VD == DT_WAVE) lds_wait<2 * (VD - 1)>(vr[d][1]);
-          else if (d + VD == DT_WAVE + 1) lds_wait<2 * (VD - 2)>(vr[d][1]);
-          else lds_wait<0>(vr[d][1]);
+        // Reads issued after fragment d: fragments d+1 .. min(d+VD-1, 7).
+        if (d + VD <= DT_WAVE) lds_wait<2 * (VD - 1)>(vr[d][1]);
+        else if (d + VD == DT_WAVE + 1) lds_wait<2 * (VD - 2)>(vr[d][1]);
+        else lds_wait<0>(vr[d][1]);
+        const vec8 va =
+            __builtin_bit_cast(vec8, u32x4{vr[d][0][0], vr[d][0][1], vr[d][1][0], vr[d][1][1]});
+#pragma unroll
+        for (int ht = 0; ht < HT_ALL; ++ht) o[d][ht] = E::mfma(va, pv[ht], o[d][ht]);
+        if (d + VD < DT_WAVE) {
+          vr[d + VD][0] = lds_read_tr_b16(sbase + offs_v[d + VD]);
+          vr[d + VD][1] = lds_read_tr_b16(sbase + offs_v[d + VD] + 16 * CKV_ROW);
         }
-        const vec8 va = __builtin_bit_cast(vec8, u32x4{vr[d][0][0], vr[d][0][1], vr[d][1][0], vr[d][1][1]});
-        o[d][0] = E::mfma(va, pv0, o[d][0]);
-        o[d][1] = E::mfma(va, pv1, o[d][1]);
-        if (d + VD + 1 < DT_WAVE) {
-          vr[d + VD + 1][0] = lds_read_tr_b16(vaddr(d + VD + 1));
-          vr[d + VD + 1][1] = lds_read_tr_b16(vaddr(d + VD + 1) + 16 * CKV_ROW);
-        }
+        if (refill) issue_one(i + 2, phys_fill, d + 1);
       }
     }
-
-    // Did any head of any wave outgrow its reference? (The pass count must
-    // be the same in all four waves: they share barriers.)
-    if (pass == 0) {
-      if (__any(m_run > m_ref + HEADROOM_LOG2) && lane == 0) *flag = 1u;
-      meet();
-      if (*(const volatile MLA_LDS uint32_t*)flag == 0u) break;
-    }
+    if (pass == 1) break;
+    meet();   // M_flag
+    if (*(const volatile MLA_LDS uint32_t*)flag == 0u) break;
+    meet();   // M_x1
+    meet();   // M_x2
   }
-
-  // ---- epilogue: swap the sums, normalise and write my dims ---------------
-  float l_tot = l_part + shfl_xor(l_part, 16);
-  l_tot += shfl_xor(l_tot, 32);
-  MLA_LDS float* xml = (MLA_LDS float*)(smem + XML);
-  if (lg == 0) xml[wave * 16 + ln] = l_tot;
-  meet();
-  const float l_pair = xml[(wave ^ 1) * 16 + ln];
-  const float inv0 = 1.0f / (half ? l_pair : l_tot);
-  const float inv1 = 1.0f / (half ? l_tot : l_pair);
+  // ---- epilogue: normalise with both token halves' sums of each head ---------
+  meet();     // M_epi
 #pragma unroll
-  for (int d = 0; d < DT_WAVE; ++d) {
-    store(0, half * DT_WAVE + d, o[d][0] * inv0);
-    store(1, half * DT_WAVE + d, o[d][1] * inv1);
+  for (int ht = 0; ht < HT_ALL; ++ht) {
+    const int w0 = ht >> 1, j = ht & 1;   // score waves w0 and w0 + 2
+    const float l = xm[(w0 * 2 + j) * 16 + ln] + xm[((w0 + 2) * 2 + j) * 16 + ln];
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int d = 0; d < DT_WAVE; ++d) store(ht, sw * DT_WAVE + d, o[d][ht] * inv);
   }
-  if (lg == 0) store_lse(half, m_ref + __builtin_amdgcn_logf(l_tot));
 }
 
 }  // namespace
