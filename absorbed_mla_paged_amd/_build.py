@@ -16,9 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla_decode.so")
 SOURCES = ["plan.cpp", "partition.hip", "partition_wide.hip", "reduce.hip"]
 HEADERS = ["internal.h", "device_common.h", "partition_common.h"]
-# Per-source extra flags. The 64-head kernel runs two waves per SIMD (256
-# registers each) and keeps its MFMA accumulators in VGPRs.
-EXTRA = {"partition_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source extra flags (none needed at present).
+EXTRA: dict[str, list[str]] = {}
 
 
 def hipcc() -> str:

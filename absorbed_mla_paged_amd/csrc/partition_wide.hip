@@ -13,26 +13,29 @@
 // With 64 heads the arithmetic per cached byte is high enough that the
 // matrix cores and LDS, not HBM, set the pace, so the layout keeps each
 // SIMD's MFMA pipe fed from two waves with different jobs:
-//  * 512 threads = 8 wave64, two per SIMD (256 registers each; the MFMA
-//    accumulators live in VGPRs). Waves 0-3 score, waves 4-7 apply values.
+//  * 512 threads = 8 wave64, two per SIMD (256 registers each). Waves 0-3
+//    score, waves 4-7 apply values. The big per-wave arrays live in AGPRs:
+//    Q (the score MFMAs' B operand) in score waves, the accumulators in
+//    value waves (each wave gets 128 VGPRs and 128 AGPRs).
 //  * Score wave s scores tokens 16 (s / 2) .. +16 of a 32-token block for
 //    heads 32 (s % 2) .. +32 of the workgroup, S^T[token, head] =
 //    K[token, :] . Q^T[:, head] on v_mfma_f32_16x16x32 (18 K-steps); Q of
-//    its 32 heads (the B operand) sits in 144 VGPRs, so each K fragment read
-//    from LDS feeds two MFMAs. It then turns its scores into 16-bit
-//    probabilities and publishes them in LDS.
+//    its 32 heads (the B operand) sits in registers (mostly AGPRs), so
+//    each K fragment read from LDS feeds two MFMAs. It then turns its scores
+//    into 16-bit probabilities (the scale folded into the exponent's fma,
+//    row sums by dot2 against ones) and publishes them in LDS.
 //  * Value wave v accumulates O^T[dim, head] for dims 128 v .. +128 and all
-//    64 heads (128 VGPRs) on v_mfma_f32_16x16x32. The MFMA result layout of
+//    64 heads (128 AGPRs) on v_mfma_f32_16x16x32. The MFMA result layout of
 //    S^T is already the B-operand layout of P^T; V^T is read from the same
 //    LDS tile with ds_read_b64_tr_b16, each fragment feeding four MFMAs.
 //  * Pipeline: in step i the score waves work on block i while the value
 //    waves apply block i - 1 (probabilities double-buffered by parity); one
 //    s_barrier per step. LDS holds a ring of 4 one-block slots (32 KB ckv +
-//    4 KB kpe); the value waves copy blocks in with global_load_lds_dwordx4
-//    (16 B per lane, a quarter of each block per wave), one copy between
-//    the MFMAs of each value fragment: a copy can hold its wave at issue for
-//    its share of the CU's vector-memory rate, and meanwhile the score wave
-//    on the same SIMD keeps the MFMA pipe busy.
+//    4 KB kpe), filled by the value waves with global_load_lds_dwordx4 (16 B
+//    per lane, a quarter of each block per wave): blocks 0 and 1 while the
+//    score waves load Q, then block i + 2 right after the meeting of step i,
+//    into the slot of block i - 2 that the meeting has just freed. Each
+//    block thus has two steps to arrive.
 //  * No rescaling inside the loop: every head's reference maximum is the
 //    maximum over the row's first block, and probabilities relative to it
 //    may grow up to 2^15 (finite in fp16 and bf16, exact to the format's
@@ -45,6 +48,7 @@
 #include "partition_common.h"
 
 #include <cmath>
+#include <type_traits>
 
 namespace mla {
 namespace part {
@@ -56,6 +60,9 @@ constexpr int HPW = 64;                         // heads per workgroup
 constexpr int SLOT = BS * (CKV_ROW + KPE_ROW);  // 36 KB per one-block slot
 constexpr int SLOT_KPE = BS * CKV_ROW;          // kpe rows after the ckv rows
 constexpr int NSLOT = 4;
+// The value waves copy blocks 0 and 1 before the first step and block
+// i + 2 right after the meeting of step i, into the slot of block i - 2.
+constexpr int NPRO = 2;
 constexpr int WAVES = 8;
 constexpr int THREADS = 64 * WAVES;
 constexpr int NSC = 4;                          // score waves (0..3)
@@ -68,9 +75,61 @@ constexpr int XM = XP + 2 * NSC * 64 * 16;      // per-head floats [wave][2][16]
 constexpr int XFLAG = XM + NSC * 32 * 4;        // "second pass needed" flag
 constexpr int LDS_BYTES = XFLAG + 16;
 constexpr float HEADROOM_LOG2 = 15.0f;          // p <= 2^15 against the reference
+// LDS fragments read ahead in the score and value MFMA loops (at most 15
+// LDS reads may be in flight: the lgkmcnt field has 4 bits).
+constexpr int KD_SCORE = 8;
+constexpr int VD_VALUE = 5;
+static_assert(KD_SCORE <= 15 && 4 + 2 * VD_VALUE <= 15, "lgkmcnt range");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 static_assert(OPS % 4 == 0 && 3 * OPW < 64, "copy split / vmcnt range");
-static_assert(OPW == DT_WAVE + 1, "one copy per value fragment, plus one");
+
+// lds_wait with a count known only after unrolling (n in 0..15).
+template <typename T>
+__device__ __forceinline__ void lds_wait_n(int n, T& v) {
+  switch (n) {
+    case 0: lds_wait<0>(v); break;
+    case 1: lds_wait<1>(v); break;
+    case 2: lds_wait<2>(v); break;
+    case 3: lds_wait<3>(v); break;
+    case 4: lds_wait<4>(v); break;
+    case 5: lds_wait<5>(v); break;
+    case 6: lds_wait<6>(v); break;
+    case 7: lds_wait<7>(v); break;
+    case 8: lds_wait<8>(v); break;
+    case 9: lds_wait<9>(v); break;
+    case 10: lds_wait<10>(v); break;
+    case 11: lds_wait<11>(v); break;
+    case 12: lds_wait<12>(v); break;
+    case 13: lds_wait<13>(v); break;
+    case 14: lds_wait<14>(v); break;
+    default: lds_wait<15>(v); break;
+  }
+}
+
+// Two probabilities rounded (to nearest even) into the 16-bit type, packed
+// low / high; and the sum of such a pair added to an fp32 total (one dot2
+// against (1, 1): exact products, one fp32 accumulation).
+template <int DT> struct Prob;
+template <> struct Prob<0> {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, h2{(_Float16)a, (_Float16)b});
+  }
+  static __device__ __forceinline__ float sum2(uint32_t p, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, p), h2{(_Float16)1.0f, (_Float16)1.0f},
+                                  acc, false);
+  }
+};
+template <> struct Prob<1> {
+  typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, h2{(__bf16)a, (__bf16)b});
+  }
+  static __device__ __forceinline__ float sum2(uint32_t p, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(h2, p),
+                                           h2{(__bf16)1.0f, (__bf16)1.0f}, acc, false);
+  }
+};
 
 // Wait until at most `later` blocks' worth of this wave's copies are still
 // in flight (copies complete in issue order).
@@ -102,11 +161,13 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
   typedef typename E::vec8 vec8;
   typedef typename E::vec4 vec4;
   typedef typename E::scalar scalar;
+  typedef Prob<DT> P;
 
   __shared__ __attribute__((aligned(1024))) char smem_raw[LDS_BYTES];
   MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  const int lane_id = lane;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 15;   // MFMA row/column inside a 16-wide tile
   const int lg = lane >> 4;   // MFMA k-group (0..3)
@@ -165,6 +226,7 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
     return;
   }
 
+  const int ntok_all = ri.tok_hi - ri.tok_lo;
   const int64_t tbl0 = (int64_t)b * max_blocks + ri.blk_lo;
   const int last_phys = a.num_blocks - 1;
   const char* ckv_base = reinterpret_cast<const char*>(a.ckv);
@@ -180,6 +242,10 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
   auto issue_one = [&](int k, int64_t phys, int i) {
     const uint32_t base = lds0 + (k & (NSLOT - 1)) * SLOT;
     const int op = sw * OPW + i;
+    // The lane offsets are recomputed per copy from an opaque lane index:
+    // hoisted out of the step loop they would hold registers throughout it.
+    int lane;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(lane) : "v"(lane_id));
     if (op < BS) {
       const uint32_t voff = ((lane & ~15) | ((lane & 15) ^ swz_ckv(op))) * 16;
       dma16s(voff, ckv_base + phys * (BS * CKV_ROW) + op * CKV_ROW, base + op * CKV_ROW);
@@ -191,23 +257,30 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
     }
   };
 
-  // Loop-invariant LDS byte offsets inside a slot. Score fragment (K-step
-  // ks): row 16 tt + ln, chunk 4 ks + lg; chunks 16 apart keep the same
-  // swizzled low bits, so ks = 4 m + kk is offs_k[kk] + 256 m. Value
-  // fragment d: dim tile 8 sw + d, rows r1 = 4 lg + ln / 4 and r1 + 16
-  // (16 KB further, same swizzle), chunk 2 (8 sw + d) + (ln / 2) % 2.
-  const int rk = 16 * tt + ln;
-  uint32_t offs_k[4], offs_p[2], offs_v[DT_WAVE];
+  // Rows past the context end may hold anything (NaN included): after its
+  // own copies of the last block have landed, a wave zeroes the ckv rows it
+  // brought in, so that 0-probability tokens add exactly 0.
+  auto zero_tail = [&](int k) {
+    const int valid = min(BS, ntok_all - k * BS);
+    if (valid < BS) {
+      for (int r = max(valid, sw * OPW); r < min(BS, (sw + 1) * OPW); ++r)
+        *(MLA_LDS u32x4*)(smem + (k & (NSLOT - 1)) * SLOT + r * CKV_ROW + lane * 16) =
+            u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+
+  // During step i the value waves fetch block i + 2 into the slot of block
+  // i - 2, free since the step's meeting. `next` holds the block table entry
+  // of the following refill, read one step ahead.
+  auto refill = [&](int i, int64_t& next) {
+    if (i + 2 >= NPRO && i + 2 < nblocks) {
+      const int64_t ph = next;
+      if (i + 3 < nblocks) next = phys_of(i + 3);
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) offs_k[kk] = rk * CKV_ROW + (((4 * kk + lg) ^ swz_ckv(rk)) * 16);
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-    offs_p[kk] = SLOT_KPE + rk * KPE_ROW + (((4 * kk + lg) ^ swz_kpe(rk)) * 16);
-  const int r1 = 4 * lg + (ln >> 2);
-#pragma unroll
-  for (int d = 0; d < DT_WAVE; ++d)
-    offs_v[d] = r1 * CKV_ROW + ((((2 * d + ((ln >> 1) & 1)) ^ swz_ckv(r1)) + 16 * sw) * 16) +
-                (ln & 1) * 8;
+      for (int c = 0; c < OPW; ++c) issue_one(i + 2, ph, c);
+    }
+  };
+
   MLA_LDS float* xm = (MLA_LDS float*)(smem + XM);   // [score wave][j][ln]
   MLA_LDS uint32_t* flag = (MLA_LDS uint32_t*)(smem + XFLAG);
   if (tid == 0) *flag = 0u;   // seen by all after the first meeting below
@@ -223,21 +296,46 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
   //   epilogue:        M_epi
   if (scorer) {
     // Q: lane (ln, lg) of head tile j holds head hwg + 32 hp + 16 j + ln,
-    // dims 32 k + 8 lg .. + 8. Score waves issue no copies, so the
-    // compiler's own wait for these loads is exact; the first block takes
-    // longer to arrive than Q.
-    vec8 q[2][KSTEPS];
+    // dims 32 k + 8 lg .. + 8. With two waves per SIMD the compiler gives
+    // each wave 128 VGPRs and 128 AGPRs, and it puts every MFMA accumulator
+    // in AGPRs (here the four score chains, 16 registers). The first KA
+    // K-steps of Q (112 registers) are loaded straight into AGPRs, which the
+    // score MFMAs read as their B operand; the rest go to VGPRs. The AGPR
+    // loads are ours, not the compiler's, so they are waited for explicitly
+    // (before any copy is issued).
+    constexpr int KA = 14;
+    u32x4 q[2][KA];
+    vec8 qv[2][KSTEPS - KA];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int64_t qr = (int64_t)b * a.heads + hwg + 32 * hp + 16 * j + ln;
-      const vec8* qa = reinterpret_cast<const vec8*>(a.q_absorbed + qr * LAT);
+      const u32x4* qa = reinterpret_cast<const u32x4*>(a.q_absorbed + qr * LAT);
+      const vec8* qav = reinterpret_cast<const vec8*>(a.q_absorbed + qr * LAT);
       const vec8* qp = reinterpret_cast<const vec8*>(a.q_pe + qr * ROPE);
 #pragma unroll
-      for (int k = 0; k < KSTEPS; ++k)
-        q[j][k] = (k < LAT / 32) ? qa[4 * k + lg] : qp[4 * (k - LAT / 32) + lg];
+      for (int k = 0; k < KA; ++k)
+        asm volatile("global_load_dwordx4 %0, %1, off" : "=a"(q[j][k]) : "v"(qa + 4 * k + lg) : "memory");
+#pragma unroll
+      for (int k = KA; k < KSTEPS; ++k)
+        qv[j][k - KA] = (k < LAT / 32) ? qav[4 * k + lg] : qp[4 * (k - LAT / 32) + lg];
     }
-    float m_ref[2] = {-INFINITY, -INFINITY};  // reference maxima of my heads
-    float m_run[2] = {-INFINITY, -INFINITY};  // max of this lane's own scores
+    wait_vmcnt<0>();
+    auto qfrag = [&](int j, int ks) {
+      return ks < KA ? __builtin_bit_cast(vec8, q[j][ks < KA ? ks : 0])
+                     : qv[j][ks < KA ? 0 : ks - KA];
+    };
+    // Loop-invariant LDS byte offsets inside a slot. Score fragment (K-step
+    // ks): row 16 tt + ln, chunk 4 ks + lg; chunks 16 apart keep the same
+    // swizzled low bits, so ks = 4 m + kk is offs_k[kk] + 256 m.
+    const int rk = 16 * tt + ln;
+    uint32_t offs_k[4], offs_p[2];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) offs_k[kk] = rk * CKV_ROW + (((4 * kk + lg) ^ swz_ckv(rk)) * 16);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+      offs_p[kk] = SLOT_KPE + rk * KPE_ROW + (((4 * kk + lg) ^ swz_kpe(rk)) * 16);
+    float m_ref[2] = {-INFINITY, -INFINITY};  // reference maxima of my heads (scaled)
+    float m_run[2] = {-INFINITY, -INFINITY};  // max of this lane's own raw scores
     float l_part[2] = {0.f, 0.f};             // this lane's share of the sums
     for (int pass = 0; pass < 2; ++pass) {
       l_part[0] = l_part[1] = 0.f;
@@ -251,7 +349,7 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
           return sbase + ((ks < LAT / 32) ? offs_k[ks & 3] + 256 * (ks >> 2)
                                           : offs_p[ks - LAT / 32]);
         };
-        constexpr int KD = 5;
+        constexpr int KD = KD_SCORE;
         f32x4 acc[2][2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -260,57 +358,68 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
         for (int ks = 0; ks < KD; ++ks) kf[ks] = lds_read_b128<vec8>(kaddr(ks));
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
-          if (ks + KD <= KSTEPS) lds_wait<KD - 1>(kf[ks]);
-          else lds_wait<0>(kf[ks]);   // tail: fewer than KD - 1 reads after ks
-          acc[0][ks & 1] = E::mfma(kf[ks], q[0][ks], acc[0][ks & 1]);
-          acc[1][ks & 1] = E::mfma(kf[ks], q[1][ks], acc[1][ks & 1]);
+          lds_wait_n(min(KD - 1, KSTEPS - 1 - ks), kf[ks]);   // reads issued after ks
+          acc[0][ks & 1] = E::mfma(kf[ks], qfrag(0, ks), acc[0][ks & 1]);
+          acc[1][ks & 1] = E::mfma(kf[ks], qfrag(1, ks), acc[1][ks & 1]);
           if (ks + KD < KSTEPS) kf[ks + KD] = lds_read_b128<vec8>(kaddr(ks + KD));
+          // Keep the MFMAs between their waits: sunk below later waits they
+          // would stop overlapping the reads.
+          __builtin_amdgcn_sched_barrier(0);
         }
         // Lane (ln, lg) holds head 32 hp + 16 j + ln at tokens 16 tt + 4 lg + e.
+        // Raw dot products: the scale goes into the exponent's fma, and
+        // maxima are tracked unscaled (the scale is positive).
         float sc[2][4];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const f32x4 sv = acc[j][0] + acc[j][1];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sc[j][e] = (16 * tt + 4 * lg + e < valid) ? sv[e] * c2 : -INFINITY;
-            m_run[j] = fmaxf(m_run[j], sc[j][e]);
-          }
+          for (int e = 0; e < 4; ++e) sc[j][e] = sv[e];
+        }
+        if (valid < BS) {   // the row's last block: hide tokens past its end
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (16 * tt + 4 * lg + e >= valid) sc[j][e] = -INFINITY;
+        }
+        float bm[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          bm[j] = fmaxf(fmaxf(sc[j][0], sc[j][1]), fmaxf(sc[j][2], sc[j][3]));
+          m_run[j] = fmaxf(m_run[j], bm[j]);
         }
         if (pass == 0 && i == 0) {
           // Reference maxima over the whole first block: both token halves
           // (score waves s and s ^ 2 hold the same heads).
-          float bm[2];
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
-            bm[j] = fmaxf(fmaxf(sc[j][0], sc[j][1]), fmaxf(sc[j][2], sc[j][3]));
             bm[j] = fmaxf(bm[j], shfl_xor(bm[j], 16));
             bm[j] = fmaxf(bm[j], shfl_xor(bm[j], 32));
             if (lg == 0) xm[(sw * 2 + j) * 16 + ln] = bm[j];
           }
           meet();   // M_ref
 #pragma unroll
-          for (int j = 0; j < 2; ++j) m_ref[j] = fmaxf(bm[j], xm[((sw ^ 2) * 2 + j) * 16 + ln]);
+          for (int j = 0; j < 2; ++j)
+            m_ref[j] = c2 * fmaxf(bm[j], xm[((sw ^ 2) * 2 + j) * 16 + ln]);
         }
         u32x4 pme;   // 16-bit P: head tile 0 tokens e = 0..3, then head tile 1
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          scalar p[4];
+          float pf[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            p[e] = static_cast<scalar>(__builtin_amdgcn_exp2f(sc[j][e] - m_ref[j]));
-            l_part[j] += static_cast<float>(p[e]);
-          }
-          pme[2 * j] = (uint32_t)__builtin_bit_cast(uint16_t, p[0]) |
-                       ((uint32_t)__builtin_bit_cast(uint16_t, p[1]) << 16);
-          pme[2 * j + 1] = (uint32_t)__builtin_bit_cast(uint16_t, p[2]) |
-                           ((uint32_t)__builtin_bit_cast(uint16_t, p[3]) << 16);
+          for (int e = 0; e < 4; ++e)
+            pf[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[j][e], c2, -m_ref[j]));
+          pme[2 * j] = P::pack2(pf[0], pf[1]);
+          pme[2 * j + 1] = P::pack2(pf[2], pf[3]);
+          l_part[j] = P::sum2(pme[2 * j + 1], P::sum2(pme[2 * j], l_part[j]));
         }
         *(MLA_LDS u32x4*)(smem + XP + (((i & 1) * NSC + sw) * 64 + lane) * 16) = pme;
       }
       if (pass == 1) break;
       // Did any score outgrow its head's reference?
-      if (__any(m_run[0] > m_ref[0] + HEADROOM_LOG2 || m_run[1] > m_ref[1] + HEADROOM_LOG2) &&
+      if (__any(c2 * m_run[0] > m_ref[0] + HEADROOM_LOG2 ||
+                c2 * m_run[1] > m_ref[1] + HEADROOM_LOG2) &&
           lane == 0)
         *flag = 1u;
       meet();   // M_flag
@@ -325,7 +434,7 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
       }
       meet();   // M_x1
 #pragma unroll
-      for (int j = 0; j < 2; ++j) m_ref[j] = fmaxf(mr[j], xm[((sw ^ 2) * 2 + j) * 16 + ln]);
+      for (int j = 0; j < 2; ++j) m_ref[j] = c2 * fmaxf(mr[j], xm[((sw ^ 2) * 2 + j) * 16 + ln]);
       meet();   // M_x2: xm is free again
     }
     // ---- epilogue: publish my heads' sums; write the LSE -------------------
@@ -349,88 +458,92 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
   // ---- value waves ----------------------------------------------------------
   // Their only vector-memory operations before the end are the copies
   // (counted by wait_blocks); the debug store above is wave 0's.
+  // LDS byte offsets of the value fragments inside a slot. Fragment d: dim
+  // tile 8 sw + d, rows r1 = 4 lg + ln / 4 and r1 + 16 (16 KB further, same
+  // swizzle), chunk c = 2 (8 sw + d) + (ln / 2) % 2 stored at c ^ swz(r1),
+  // i.e. at 16 sw + 2 (d ^ (swz / 2)) + ((ln / 2) ^ swz) % 2. They are
+  // rebuilt each step from an opaque copy of swz (three VALU operations per
+  // fragment) instead of being held in eight registers.
+  const int r1 = 4 * lg + (ln >> 2);
+  const int swz_v = swz_ckv(r1);
+  const uint32_t vrow = r1 * CKV_ROW + (16 * sw + (((ln >> 1) ^ swz_v) & 1)) * 16 + (ln & 1) * 8;
   f32x4 o[DT_WAVE][HT_ALL];
+  // Block kb's values into o. The first block of a pass starts the
+  // accumulators from a zero C operand instead of a separate zeroing (which
+  // the compiler would keep apart from the accumulators and copy around).
+  auto apply = [&](int kb, auto first_block) {
+    constexpr bool first = decltype(first_block)::value;
+    const uint32_t sbase = lds0 + (kb & (NSLOT - 1)) * SLOT;
+    int sh;
+    asm volatile("v_lshrrev_b32 %0, 1, %1" : "=v"(sh) : "v"(swz_v));   // swz / 2, opaque
+    const uint32_t vbase = sbase + vrow;
+    auto vaddr = [&](int d) { return vbase + 32u * (uint32_t)(d ^ sh); };
+    // P^T B operand of head tile ht (pair ht / 2, tile ht % 2): tokens
+    // 4 lg + e from score wave ht / 2, 16 + 4 lg + e from score wave ht / 2 + 2.
+    const uint32_t pbase = lds0 + XP + ((kb & 1) * NSC * 64 + lane) * 16;
+    u32x4 pw[NSC];
+#pragma unroll
+    for (int v = 0; v < NSC; ++v) pw[v] = lds_read_b128<u32x4>(pbase + v * 64 * 16);
+    constexpr int VD = VD_VALUE;
+    u32x2 vr[DT_WAVE][2];
+#pragma unroll
+    for (int d = 0; d < VD; ++d) {
+      vr[d][0] = lds_read_tr_b16(vaddr(d));
+      vr[d][1] = lds_read_tr_b16(vaddr(d) + 16 * CKV_ROW);
+    }
+    lds_wait<2 * VD>(pw[3]);
+    vec8 pv[HT_ALL];
+#pragma unroll
+    for (int ht = 0; ht < HT_ALL; ++ht) {
+      const u32x4 lo = pw[ht >> 1], hi = pw[(ht >> 1) + 2];
+      const int jj = 2 * (ht & 1);
+      pv[ht] = __builtin_bit_cast(vec8, u32x4{lo[jj], lo[jj + 1], hi[jj], hi[jj + 1]});
+    }
+#pragma unroll
+    for (int d = 0; d < DT_WAVE; ++d) {
+      // Reads issued after fragment d: fragments d+1 .. min(d+VD-1, 7).
+      lds_wait_n(2 * min(VD - 1, DT_WAVE - 1 - d), vr[d][1]);
+      const vec8 va =
+          __builtin_bit_cast(vec8, u32x4{vr[d][0][0], vr[d][0][1], vr[d][1][0], vr[d][1][1]});
+#pragma unroll
+      for (int ht = 0; ht < HT_ALL; ++ht)
+        o[d][ht] = E::mfma(va, pv[ht], first ? f32x4{0.f, 0.f, 0.f, 0.f} : o[d][ht]);
+      if (d + VD < DT_WAVE) {
+        vr[d + VD][0] = lds_read_tr_b16(vaddr(d + VD));
+        vr[d + VD][1] = lds_read_tr_b16(vaddr(d + VD) + 16 * CKV_ROW);
+      }
+      __builtin_amdgcn_sched_barrier(0);   // as in the score loop
+    }
+  };
   for (int pass = 0; pass < 2; ++pass) {
-    // An opaque zero: a literal one would be hoisted out of the pass loop
-    // and kept alive next to the accumulators.
-    float zero;
-    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
-#pragma unroll
-    for (int d = 0; d < DT_WAVE; ++d)
-#pragma unroll
-      for (int ht = 0; ht < HT_ALL; ++ht) o[d][ht] = f32x4{zero, zero, zero, zero};
-    for (int k = 0; k < NSLOT && k < nblocks; ++k) {
+    // Blocks 0 and 1 before the first step (the rest during the steps).
+    const int npro = min(NPRO, nblocks);
+    for (int k = 0; k < npro; ++k) {
       const int64_t ph = phys_of(k);
 #pragma unroll
       for (int c = 0; c < OPW; ++c) issue_one(k, ph, c);
     }
-    int64_t phys_next = nblocks > NSLOT ? phys_of(NSLOT) : 0;
-
-    // Step i: apply block i - 1 (i >= 1) while the score waves score block i.
-    for (int i = 0; i <= nblocks; ++i) {
+    // Start of step i: block i must be in LDS (my later copies, of blocks
+    // i + 1 .. last, may still be in flight), then M_step(i), then the copy
+    // of block i + 2.
+    int64_t phys_next = nblocks > NPRO ? phys_of(NPRO) : 0;
+    auto step_begin = [&](int i) {
       if (i < nblocks) {
-        // Block i must be in LDS when the step starts; copies of blocks up
-        // to min(max(3, i + 1), nblocks - 1) were issued before this point.
-        wait_blocks(min(max(NSLOT - 1, i + 1), nblocks - 1) - i);
-        const int valid = min(BS, ntok - i * BS);
-        if (valid < BS) {
-          // Rows past the context end may hold anything (NaN included): zero
-          // the ckv rows this wave brought in, so that 0-probability tokens
-          // add exactly 0.
-          for (int r = max(valid, sw * OPW); r < min(BS, (sw + 1) * OPW); ++r)
-            *(MLA_LDS u32x4*)(smem + (i & (NSLOT - 1)) * SLOT + r * CKV_ROW + lane * 16) =
-                u32x4{0u, 0u, 0u, 0u};
-        }
+        const int last = min(max(npro - 1, i + 1), nblocks - 1);
+        wait_blocks(last - i);
+        if (i == nblocks - 1) zero_tail(i);
       }
-      meet();                                   // M_step(i)
-      if (pass == 0 && i == 0) meet();          // M_ref
-      if (i < 1) continue;
-      // ---- values: block i - 1, dims 128 sw .. +128, all 64 heads -------------
-      const int kb = i - 1;
-      const uint32_t sbase = lds0 + (kb & (NSLOT - 1)) * SLOT;
-      // Refill the slot of block i - 2 (free since this step's meeting) with
-      // block i + 2, one copy per value fragment.
-      const bool refill = i >= 2 && i + 2 < nblocks;
-      const int64_t phys_fill = phys_next;
-      if (refill && i + 3 < nblocks) phys_next = phys_of(i + 3);
-      if (refill) issue_one(i + 2, phys_fill, 0);
-      // P^T B operand of head tile ht (pair ht / 2, tile ht % 2): tokens
-      // 4 lg + e from score wave ht / 2, 16 + 4 lg + e from score wave ht / 2 + 2.
-      const uint32_t pbase = lds0 + XP + ((kb & 1) * NSC * 64 + lane) * 16;
-      u32x4 pw[NSC];
-#pragma unroll
-      for (int v = 0; v < NSC; ++v) pw[v] = lds_read_b128<u32x4>(pbase + v * 64 * 16);
-      constexpr int VD = 3;   // value fragments read ahead
-      u32x2 vr[DT_WAVE][2];
-#pragma unroll
-      for (int d = 0; d < VD; ++d) {
-        vr[d][0] = lds_read_tr_b16(sbase + offs_v[d]);
-        vr[d][1] = lds_read_tr_b16(sbase + offs_v[d] + 16 * CKV_ROW);
-      }
-      lds_wait<2 * VD>(pw[3]);
-      vec8 pv[HT_ALL];
-#pragma unroll
-      for (int ht = 0; ht < HT_ALL; ++ht) {
-        const u32x4 lo = pw[ht >> 1], hi = pw[(ht >> 1) + 2];
-        const int jj = 2 * (ht & 1);
-        pv[ht] = __builtin_bit_cast(vec8, u32x4{lo[jj], lo[jj + 1], hi[jj], hi[jj + 1]});
-      }
-#pragma unroll
-      for (int d = 0; d < DT_WAVE; ++d) {
-        // Reads issued after fragment d: fragments d+1 .. min(d+VD-1, 7).
-        if (d + VD <= DT_WAVE) lds_wait<2 * (VD - 1)>(vr[d][1]);
-        else if (d + VD == DT_WAVE + 1) lds_wait<2 * (VD - 2)>(vr[d][1]);
-        else lds_wait<0>(vr[d][1]);
-        const vec8 va =
-            __builtin_bit_cast(vec8, u32x4{vr[d][0][0], vr[d][0][1], vr[d][1][0], vr[d][1][1]});
-#pragma unroll
-        for (int ht = 0; ht < HT_ALL; ++ht) o[d][ht] = E::mfma(va, pv[ht], o[d][ht]);
-        if (d + VD < DT_WAVE) {
-          vr[d + VD][0] = lds_read_tr_b16(sbase + offs_v[d + VD]);
-          vr[d + VD][1] = lds_read_tr_b16(sbase + offs_v[d + VD] + 16 * CKV_ROW);
-        }
-        if (refill) issue_one(i + 2, phys_fill, d + 1);
-      }
+      meet();
+      if (i < nblocks) refill(i, phys_next);
+    };
+    // Step i applies block i - 1 while the score waves score block i.
+    step_begin(0);
+    if (pass == 0) meet();   // M_ref
+    step_begin(1);
+    apply(0, std::true_type{});
+    for (int i = 2; i <= nblocks; ++i) {
+      step_begin(i);
+      apply(i - 1, std::false_type{});
     }
     if (pass == 1) break;
     meet();   // M_flag
