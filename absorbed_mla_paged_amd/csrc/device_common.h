@@ -103,7 +103,7 @@ __device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_
 // in flight ahead of the MFMAs consuming them (the compiler's own schedule
 // keeps one or two). The compiler does not count these reads, so every use
 // must be preceded by lds_wait<N>(value), N = the number of LDS reads issued
-// after this one. LDS operations complete in order; any other LDS or scalar
+// after this one; a wait makes only the values passed to it safe to use. LDS operations complete in order; any other LDS or scalar
 // operation the compiler puts in between only makes such a wait stricter.
 template <typename T>
 __device__ __forceinline__ T lds_read_b128(uint32_t addr) {
@@ -124,6 +124,81 @@ __device__ __forceinline__ void lds_wait(T& v) {
   static_assert(N >= 0 && N < 16, "lgkmcnt field is 4 bits");
   asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(N));
 }
+
+// The same wait guarding two values (both are ready after it).
+template <int N, typename T, typename U>
+__device__ __forceinline__ void lds_wait(T& v, U& w) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt field is 4 bits");
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(v), "+v"(w) : "n"(N));
+}
+
+// lds_wait with a count known only after unrolling (n in 0..15).
+template <typename T>
+__device__ __forceinline__ void lds_wait_n(int n, T& v) {
+  switch (n) {
+    case 0: lds_wait<0>(v); break;
+    case 1: lds_wait<1>(v); break;
+    case 2: lds_wait<2>(v); break;
+    case 3: lds_wait<3>(v); break;
+    case 4: lds_wait<4>(v); break;
+    case 5: lds_wait<5>(v); break;
+    case 6: lds_wait<6>(v); break;
+    case 7: lds_wait<7>(v); break;
+    case 8: lds_wait<8>(v); break;
+    case 9: lds_wait<9>(v); break;
+    case 10: lds_wait<10>(v); break;
+    case 11: lds_wait<11>(v); break;
+    case 12: lds_wait<12>(v); break;
+    case 13: lds_wait<13>(v); break;
+    case 14: lds_wait<14>(v); break;
+    default: lds_wait<15>(v); break;
+  }
+}
+template <typename T, typename U>
+__device__ __forceinline__ void lds_wait_n(int n, T& v, U& w) {
+  switch (n) {
+    case 0: lds_wait<0>(v, w); break;
+    case 1: lds_wait<1>(v, w); break;
+    case 2: lds_wait<2>(v, w); break;
+    case 3: lds_wait<3>(v, w); break;
+    case 4: lds_wait<4>(v, w); break;
+    case 5: lds_wait<5>(v, w); break;
+    case 6: lds_wait<6>(v, w); break;
+    case 7: lds_wait<7>(v, w); break;
+    case 8: lds_wait<8>(v, w); break;
+    case 9: lds_wait<9>(v, w); break;
+    case 10: lds_wait<10>(v, w); break;
+    case 11: lds_wait<11>(v, w); break;
+    case 12: lds_wait<12>(v, w); break;
+    case 13: lds_wait<13>(v, w); break;
+    case 14: lds_wait<14>(v, w); break;
+    default: lds_wait<15>(v, w); break;
+  }
+}
+
+// 16-byte stores into a wave-uniform region, written through the L2 to
+// device scope (sc1): the lines are not left dirty in this XCD's L2, so the
+// release at the end of the kernel has less to write back, and readers on
+// other XCDs find them in memory. A buffer store from the builtin (not
+// inline asm) lets the compiler keep the data registers untouched until the
+// store has read them. Offsets at or past `bytes` are dropped.
+struct WtRegion {
+  __amdgpu_buffer_rsrc_t rsrc;
+  __device__ WtRegion(void* base, uint32_t bytes)
+      : rsrc(__builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, 0x00020000)) {}
+  static constexpr int kSc1 = 16;   // cache-policy bit: device-scope write-through
+  __device__ void store(uint32_t byte_off, f32x4 v) const {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rsrc, (int)byte_off, 0,
+                                           kSc1);
+  }
+  __device__ void store(uint32_t byte_off, u32x2 v) const {
+    __builtin_amdgcn_raw_buffer_store_b64(v, rsrc, (int)byte_off, 0, kSc1);
+  }
+  __device__ void store(uint32_t byte_off, float v) const {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rsrc, (int)byte_off, 0,
+                                          kSc1);
+  }
+};
 
 // Read-only int32 metadata (block table, plan arrays) through the constant
 // address space: uniform loads then become scalar (s_load, counted by

@@ -41,6 +41,7 @@
 #include "partition_common.h"
 
 #include <cmath>
+#include <type_traits>
 
 namespace mla {
 namespace {
@@ -98,6 +99,7 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
   const int hg = sl % groups;
   const int u = (sl / groups) * 8 + (L & 7);
   if (u >= slots) return;
+
   const int b = u / rows_per_req;
   const int x = u % rows_per_req;
 
@@ -105,10 +107,10 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
   const int64_t qrow0 = (int64_t)b * a.heads + head0;   // first (b, head) row
   const int my_head = head0 + ln;
 
-  // Q (compute waves): issued first, its address needs no metadata. B
-  // operand of the score product: lane (ln, lg) holds head head0 + ln, dims
-  // 32 k + 8 lg .. + 8. Compute waves issue no copies, so the compiler's
-  // own wait for Q is exact.
+  // Q (compute waves; its address needs no metadata). B operand of the
+  // score product: lane (ln, lg) holds head head0 + ln, dims 32 k + 8 lg ..
+  // + 8. Compute waves issue no copies, so the compiler's own wait for Q is
+  // exact.
   vec8 q[KSTEPS];
   if (!copier) {
     const vec8* qa = reinterpret_cast<const vec8*>(a.q_absorbed + (qrow0 + ln) * LAT);
@@ -149,6 +151,15 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
   const int nblocks = cdiv(tok_hi - tok_lo, BS);   // non-empty blocks
   const int nst = cdiv(nblocks, 2);                 // stages
 
+  // LDS counters, zeroed behind one barrier (it waits for the scalar loads
+  // above, never for Q or the table).
+  MLA_LDS uint32_t* ready = (MLA_LDS uint32_t*)(smem + XCNT);
+  MLA_LDS uint32_t* freed = ready + 2;
+  MLA_LDS uint32_t* issued = ready + 4;
+  MLA_LDS uint32_t* scored = ready + 5;  // compute waves: score tiles written
+  if (tid < 6) ready[tid] = 0u;
+  __syncthreads();
+
   if (nst <= 0) {
     // No visible token: zero output, lse2 = -inf.
     if (copier) return;
@@ -176,13 +187,6 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
     }
     return;
   }
-
-  MLA_LDS uint32_t* ready = (MLA_LDS uint32_t*)(smem + XCNT);
-  MLA_LDS uint32_t* freed = ready + 2;
-  MLA_LDS uint32_t* issued = ready + 4;
-  MLA_LDS uint32_t* scored = ready + 5;  // compute waves: score tiles written
-  if (tid < 6) ready[tid] = 0u;
-  __syncthreads();
 
   if (copier) {
     // ---- copy waves: pair `slot` serves stages slot, slot + 2, ... ------
@@ -256,65 +260,138 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
   float m_ref = -INFINITY;  // reference maximum of my head, base 2
   float l_part = 0.f;       // this lane's 16 token slots of the running sum
   const float c2 = a.scale_log2;
+  const int tt = wave;      // my score tile: tokens 16 tt .. 16 tt + 15 of a stage
+
+  // LDS byte offsets inside a stage. Score fragment (K-step ks): row
+  // 16 tt + ln, chunk 4 ks + lg; chunks 16 apart keep the same swizzled low
+  // bits, so ks = 4 m + kk sits at offs_k[kk] + 256 m. Value fragment
+  // (K-step kb, dim tile 8 tt + dt): rows r1 = 32 kb + 4 lg + ln / 4 and
+  // r1 + 16 (same swizzle), chunk 2 (8 tt + dt) + (ln / 2) % 2, i.e. at
+  // voff + 32 KB kb + 32 (dt ^ (swz / 2)).
+  const int rk = 16 * tt + ln;
+  uint32_t offs_k[4], offs_p[2];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) offs_k[kk] = rk * CKV_ROW + (((4 * kk + lg) ^ swz_ckv(rk)) * 16);
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+    offs_p[kk] = ST_KPE + rk * KPE_ROW + (((4 * kk + lg) ^ swz_kpe(rk)) * 16);
+  const int rv = 4 * lg + (ln >> 2);
+  const int swz_v = swz_ckv(rv);
+  const uint32_t voff = rv * CKV_ROW + (ln & 1) * 8 + 16 * (16 * tt + (((ln >> 1) ^ swz_v) & 1));
+  const int vsh = swz_v >> 1;
+
+  // Normalise and write this workgroup's output: 16 heads x my 128 dims
+  // (fp32 partial of row `row`, or the rounded output when the request is a
+  // single row) and the base-2 LSE, all written through the L2 from
+  // wave-uniform regions (32 KB of partials per workgroup: the stores are
+  // bound by the CU's store rate).
+  auto finish = [&]() {
+    float l_tot = l_part + shfl_xor(l_part, 16);
+    l_tot = l_tot + shfl_xor(l_tot, 32);
+    const float inv = 1.0f / l_tot;
+    const int dbase = wave * DT_PER_WAVE * 16 + lg * 4;
+    const uint32_t e_off = (uint32_t)(ln * LAT + dbase);   // element offset in the region
+    if (direct) {
+      const WtRegion dst(reinterpret_cast<uint16_t*>(a.out) + ((int64_t)b * a.heads + head0) * LAT,
+                         HG * LAT * 2);
+#pragma unroll
+      for (int dt = 0; dt < DT_PER_WAVE; ++dt) {
+        vec4 hv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hv[j] = static_cast<scalar>(o[dt][j] * inv);
+        dst.store(e_off * 2 + dt * 32, __builtin_bit_cast(u32x2, hv));
+      }
+    } else {
+      const WtRegion dst(a.partial_out + ((int64_t)row * a.heads + head0) * LAT,
+                         HG * LAT * 4);
+#pragma unroll
+      for (int dt = 0; dt < DT_PER_WAVE; ++dt) dst.store(e_off * 4 + dt * 64, o[dt] * inv);
+    }
+    if (wave == 0) {
+      // Lanes with the same head write the same value.
+      float* lp = direct ? a.lse2_out : a.partial_lse2;
+      const WtRegion lse(lp ? lp + (int64_t)(direct ? b : row) * a.heads + head0 : nullptr,
+                         lp ? HG * 4 : 0);
+      lse.store((uint32_t)ln * 4, m_ref + __builtin_amdgcn_logf(l_tot));
+    }
+  };
 
   for (int k = 0; k < nst; ++k) {
     const int slot = k & 1;
-    const MLA_LDS char* stg = smem + slot * STAGE;
+    const uint32_t sbase = lds_addr(smem) + slot * STAGE;
     const int valid = min(ST_TOK, tok_hi - (tok_lo + k * ST_TOK));
     wait_counter(ready + slot, 2 * (k / 2 + 1));
 
-    // Scores of my tile: tokens 16 wave .. 16 wave + 15 of the stage.
-    const int tt = wave;
+    // ---- scores of my tile: all 18 K fragments read ahead (14 in flight)
     float xs[4];
     if (16 * tt < valid) {
-      f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-      const int r = tt * 16 + ln;
-      const int sw = swz_ckv(r), swk = swz_kpe(r);
-      // Fragments are read six K-steps at a time, ahead of their MFMAs.
-      constexpr int KG = 6;
+      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      auto kaddr = [&](int ks) {
+        return sbase + ((ks < LAT / 32) ? offs_k[ks & 3] + 256 * (ks >> 2) : offs_p[ks - LAT / 32]);
+      };
+      constexpr int KD = 14;
+      vec8 kf[KSTEPS];
 #pragma unroll
-      for (int k0 = 0; k0 < KSTEPS; k0 += KG) {
-        vec8 kf[KG];
+      for (int ks = 0; ks < KD; ++ks) kf[ks] = lds_read_b128<vec8>(kaddr(ks));
 #pragma unroll
-        for (int i = 0; i < KG; ++i) {
-          const int kk = k0 + i;
-          const MLA_LDS char* pk = (kk < LAT / 32)
-              ? stg + r * CKV_ROW + (((4 * kk + lg) ^ sw) * 16)
-              : stg + ST_KPE + r * KPE_ROW + (((4 * (kk - LAT / 32) + lg) ^ swk) * 16);
-          kf[i] = *(const MLA_LDS vec8*)pk;
-        }
-#pragma unroll
-        for (int i = 0; i < KG; ++i) {
-          if (i & 1) acc1 = E::mfma(kf[i], q[k0 + i], acc1);
-          else acc0 = E::mfma(kf[i], q[k0 + i], acc0);
-        }
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        lds_wait_n(min(KD - 1, KSTEPS - 1 - ks), kf[ks]);
+        acc[ks & 1] = E::mfma(kf[ks], q[ks], acc[ks & 1]);
+        if (ks + KD < KSTEPS) kf[ks + KD] = lds_read_b128<vec8>(kaddr(ks + KD));
+        __builtin_amdgcn_sched_barrier(0);   // keep each MFMA between its waits
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int tk = 16 * tt + 4 * lg + j;
-        xs[j] = (tk < valid) ? (acc0[j] + acc1[j]) * c2 : -INFINITY;
+        xs[j] = (tk < valid) ? (acc[0][j] + acc[1][j]) * c2 : -INFINITY;
       }
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) xs[j] = -INFINITY;
     }
     // Publish my tile, meet, read all four tiles (same lane, same layout).
-    MLA_LDS char* sbuf = smem + XS + (k & 1) * (CWAVES * 64 * 16);
-    *(MLA_LDS f32x4*)(sbuf + (tt * 64 + lane) * 16) = f32x4{xs[0], xs[1], xs[2], xs[3]};
+    const uint32_t sbuf = lds_addr(smem) + XS + (k & 1) * (CWAVES * 64 * 16);
+    *(MLA_LDS f32x4*)(smem + XS + (k & 1) * (CWAVES * 64 * 16) + (tt * 64 + lane) * 16) =
+        f32x4{xs[0], xs[1], xs[2], xs[3]};
     bump_counter(scored, lane);
     wait_counter(scored, CWAVES * (k + 1));
+    f32x4 tile[CWAVES];
+#pragma unroll
+    for (int t = 0; t < CWAVES; ++t) tile[t] = lds_read_b128<f32x4>(sbuf + (t * 64 + lane) * 16);
+
+    lds_wait<0>(tile[0], tile[1]);
+    lds_wait<0>(tile[2], tile[3]);
     float sc[16];
 #pragma unroll
-    for (int t = 0; t < CWAVES; ++t) {
-      const f32x4 v = *(const MLA_LDS f32x4*)(sbuf + (t * 64 + lane) * 16);
+    for (int t = 0; t < CWAVES; ++t)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sc[4 * t + j] = v[j];
-    }
+      for (int j = 0; j < 4; ++j) sc[4 * t + j] = tile[t][j];
     float bm = sc[0];
 #pragma unroll
     for (int j = 1; j < 16; ++j) bm = fmaxf(bm, sc[j]);
     bm = fmaxf(bm, shfl_xor(bm, 16));
     bm = fmaxf(bm, shfl_xor(bm, 32));
+    // Consume the shuffled maximum here, so that the compiler's wait for
+    // the shuffles (lgkmcnt(0)) comes before the value reads below.
+    asm volatile("" : "+v"(bm));
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Values, K-step kb = tokens 32 kb .. 32 kb + 31, dim tiles 8 tt + dt:
+    // fragment f = 8 kb + dt. Their transposed reads do not depend on the
+    // probabilities, so the first VD fragments are issued before the
+    // exponentials (after the cross-lane maximum, whose LDS-routed shuffles
+    // the compiler waits for with lgkmcnt(0)). A one-block stage has one
+    // K-step (its second half is never read).
+    constexpr int VD = 7;   // fragments in flight: 2 VD <= 15
+    auto vaddr = [&](int f) {
+      return sbase + voff + (f >> 3) * (BS * CKV_ROW) + 32u * (uint32_t)((f & 7) ^ vsh);
+    };
+    u32x2 vr[2 * DT_PER_WAVE][2];
+#pragma unroll
+    for (int f = 0; f < VD; ++f) {
+      vr[f][0] = lds_read_tr_b16(vaddr(f));
+      vr[f][1] = lds_read_tr_b16(vaddr(f) + 16 * CKV_ROW);
+    }
     const bool need = bm > m_ref + RESCALE_LOG2;
     if (__any(need)) {
       const float m_new = need ? bm : m_ref;
@@ -324,67 +401,38 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
       l_part *= alpha;
       m_ref = m_new;
     }
-    // Values, K-step kb = tokens 32 kb .. 32 kb + 31. The B operand of lane
-    // (ln, lg) is P of head ln at tokens 32 kb + 4 lg + j and
-    // 32 kb + 16 + 4 lg + j (j < 4): scores sc[8 kb + j]. The A operand is
-    // dim 16 dtg + ln of the same tokens, read transposed from the tile.
+    // The B operand of lane (ln, lg) at K-step kb is P of head ln at tokens
+    // 32 kb + 4 lg + j and 32 kb + 16 + 4 lg + j (j < 4): scores sc[8 kb + j].
     // Masked tokens give p = 0 exactly.
-    const int ksteps_pv = valid > BS ? 2 : 1;
+    vec8 pv[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (kb < ksteps_pv) {
-        vec8 pv;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const scalar pj = static_cast<scalar>(__builtin_amdgcn_exp2f(sc[8 * kb + j] - m_ref));
-          pv[j] = pj;
-          l_part += static_cast<float>(pj);
-        }
-        const int r1 = kb * BS + 4 * lg + (ln >> 2);
-        const int r2 = r1 + 16;
-        const MLA_LDS char* v1row = stg + r1 * CKV_ROW + (ln & 1) * 8;
-        const MLA_LDS char* v2row = stg + r2 * CKV_ROW + (ln & 1) * 8;
-        const int s1 = swz_ckv(r1), s2 = swz_ckv(r2);
-#pragma unroll
-        for (int dt = 0; dt < DT_PER_WAVE; ++dt) {
-          const int dtg = wave * DT_PER_WAVE + dt;
-          const int cpos = 2 * dtg + ((ln >> 1) & 1);
-          const vec4 v1 = E::tr_read(v1row + ((cpos ^ s1) * 16));
-          const vec4 v2 = E::tr_read(v2row + ((cpos ^ s2) * 16));
-          o[dt] = E::mfma(__builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7), pv, o[dt]);
-        }
+      for (int j = 0; j < 8; ++j) {
+        const scalar pj = static_cast<scalar>(__builtin_amdgcn_exp2f(sc[8 * kb + j] - m_ref));
+        pv[kb][j] = pj;
+        l_part += static_cast<float>(pj);
       }
-    }
+    auto values = [&](auto nfrag_tag) {
+      constexpr int NF = decltype(nfrag_tag)::value;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        lds_wait_n(2 * min(VD - 1, NF - 1 - f), vr[f][0], vr[f][1]);
+        const vec8 va =
+            __builtin_bit_cast(vec8, u32x4{vr[f][0][0], vr[f][0][1], vr[f][1][0], vr[f][1][1]});
+        o[f & 7] = E::mfma(va, pv[f >> 3], o[f & 7]);
+        if (f + VD < NF) {
+          vr[f + VD][0] = lds_read_tr_b16(vaddr(f + VD));
+          vr[f + VD][1] = lds_read_tr_b16(vaddr(f + VD) + 16 * CKV_ROW);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    if (valid > BS) values(std::integral_constant<int, 2 * DT_PER_WAVE>{});
+    else values(std::integral_constant<int, DT_PER_WAVE>{});
     bump_counter(freed + slot, lane);
   }
-
-  // ---- epilogue: normalise and write -------------------------------------
-  float l_tot = l_part + shfl_xor(l_part, 16);
-  l_tot = l_tot + shfl_xor(l_tot, 32);
-  const float inv = 1.0f / l_tot;
-#pragma unroll
-  for (int dt = 0; dt < DT_PER_WAVE; ++dt) {
-    const int d0 = (wave * DT_PER_WAVE + dt) * 16 + lg * 4;
-    const f32x4 v = o[dt] * inv;
-    if (direct) {
-      uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)b * a.heads + my_head) * LAT + d0;
-      vec4 hv;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) hv[j] = static_cast<scalar>(v[j]);
-      *reinterpret_cast<vec4*>(dst) = hv;
-    } else {
-      float* dst = a.partial_out + ((int64_t)row * a.heads + my_head) * LAT + d0;
-      *reinterpret_cast<f32x4*>(dst) = v;
-    }
-  }
-  if (wave == 0 && lg == 0) {
-    const float lse2 = m_ref + __builtin_amdgcn_logf(l_tot);
-    if (direct) {
-      if (a.lse2_out) a.lse2_out[(int64_t)b * a.heads + my_head] = lse2;
-    } else {
-      a.partial_lse2[(int64_t)row * a.heads + my_head] = lse2;
-    }
-  }
+  finish();
   if (a.debug_ranges && hg == 0 && tid == 0) {
     a.debug_ranges[2 * row] = tok_lo;
     a.debug_ranges[2 * row + 1] = tok_hi;

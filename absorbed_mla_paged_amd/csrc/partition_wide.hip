@@ -83,29 +83,6 @@ static_assert(KD_SCORE <= 15 && 4 + 2 * VD_VALUE <= 15, "lgkmcnt range");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 static_assert(OPS % 4 == 0 && 3 * OPW < 64, "copy split / vmcnt range");
 
-// lds_wait with a count known only after unrolling (n in 0..15).
-template <typename T>
-__device__ __forceinline__ void lds_wait_n(int n, T& v) {
-  switch (n) {
-    case 0: lds_wait<0>(v); break;
-    case 1: lds_wait<1>(v); break;
-    case 2: lds_wait<2>(v); break;
-    case 3: lds_wait<3>(v); break;
-    case 4: lds_wait<4>(v); break;
-    case 5: lds_wait<5>(v); break;
-    case 6: lds_wait<6>(v); break;
-    case 7: lds_wait<7>(v); break;
-    case 8: lds_wait<8>(v); break;
-    case 9: lds_wait<9>(v); break;
-    case 10: lds_wait<10>(v); break;
-    case 11: lds_wait<11>(v); break;
-    case 12: lds_wait<12>(v); break;
-    case 13: lds_wait<13>(v); break;
-    case 14: lds_wait<14>(v); break;
-    default: lds_wait<15>(v); break;
-  }
-}
-
 // Two probabilities rounded (to nearest even) into the 16-bit type, packed
 // low / high; and the sum of such a pair added to an fp32 total (one dot2
 // against (1, 1): exact products, one fp32 accumulation).
@@ -198,16 +175,15 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
       *reinterpret_cast<vec4*>(reinterpret_cast<uint16_t*>(a.out) +
                                ((int64_t)b * a.heads + h) * LAT + d0) = hv;
     } else {
-      *reinterpret_cast<f32x4*>(a.partial_out + ((int64_t)row * a.heads + h) * LAT + d0) = v;
+      // Written through the L2, from this workgroup's 64-head region of the row.
+      const WtRegion part(a.partial_out + ((int64_t)row * a.heads + hwg) * LAT, HPW * LAT * 4);
+      part.store((uint32_t)((16 * ht + ln) * LAT + d0) * 4, v);
     }
   };
   auto store_lse = [&](int h_local, float v) {
     const int64_t i = (int64_t)(direct ? b : row) * a.heads + hwg + h_local;
-    if (direct) {
-      if (a.lse2_out) a.lse2_out[i] = v;
-    } else {
-      a.partial_lse2[i] = v;
-    }
+    float* lp = direct ? a.lse2_out : a.partial_lse2;
+    if (lp) __hip_atomic_store(lp + i, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
   if (a.debug_ranges && hg == 0 && tid == 0) {
     a.debug_ranges[2 * row] = ri.tok_lo;
@@ -320,6 +296,12 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
         qv[j][k - KA] = (k < LAT / 32) ? qav[4 * k + lg] : qp[4 * (k - LAT / 32) + lg];
     }
     wait_vmcnt<0>();
+    // Tie the AGPR halves of Q to that wait (the compiler does not know the
+    // asm loads are asynchronous; a use is safe only after an ordered asm).
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int k = 0; k < KA; ++k) asm volatile("" : "+a"(q[j][k]));
     auto qfrag = [&](int j, int ks) {
       return ks < KA ? __builtin_bit_cast(vec8, q[j][ks < KA ? ks : 0])
                      : qv[j][ks < KA ? 0 : ks - KA];
@@ -491,7 +473,8 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
       vr[d][0] = lds_read_tr_b16(vaddr(d));
       vr[d][1] = lds_read_tr_b16(vaddr(d) + 16 * CKV_ROW);
     }
-    lds_wait<2 * VD>(pw[3]);
+    lds_wait<2 * VD>(pw[0], pw[1]);
+    lds_wait<2 * VD>(pw[2], pw[3]);
     vec8 pv[HT_ALL];
 #pragma unroll
     for (int ht = 0; ht < HT_ALL; ++ht) {
@@ -502,7 +485,7 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
 #pragma unroll
     for (int d = 0; d < DT_WAVE; ++d) {
       // Reads issued after fragment d: fragments d+1 .. min(d+VD-1, 7).
-      lds_wait_n(2 * min(VD - 1, DT_WAVE - 1 - d), vr[d][1]);
+      lds_wait_n(2 * min(VD - 1, DT_WAVE - 1 - d), vr[d][0], vr[d][1]);
       const vec8 va =
           __builtin_bit_cast(vec8, u32x4{vr[d][0][0], vr[d][0][1], vr[d][1][0], vr[d][1][1]});
 #pragma unroll

@@ -12,9 +12,11 @@
 // One workgroup handles (b, h, a 32-dim slice): 32 row lanes x 8 threads,
 // each thread owning 4 consecutive dims (one 16-byte load per row), so a
 // row's slice is one 128-byte line. Row lane k takes rows k, k+32, ... in
-// order, with 8 rows' loads issued before any is used, so a request's whole
-// partial set is in flight at once; the 32 row-lane sums are then added in a
-// fixed order, so the result is bit-identical run to run.
+// order, with 8 rows' loads (slice and lse2) issued before any is used, so
+// a request's whole partial set is in flight at once, in a single round
+// trip. Each row lane keeps its own running maximum, weighted sum and
+// weight; the 32 row lanes are then merged in a fixed tree order (lane
+// shuffles, then the four waves), so the result is bit-identical run to run.
 #include "device_common.h"
 #include "internal.h"
 
@@ -44,22 +46,11 @@ struct ReduceArgs {
   int32_t total_rows;
 };
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
-}
-
 template <int DT>
 __global__ __launch_bounds__(THREADS) void reduce_kernel(ReduceArgs a) {
   typedef Elem<DT> E;
-  __shared__ float red[THREADS / 64];
-  __shared__ f32x4 part[RL][TPR];
+  __shared__ f32x4 part[THREADS / 64][TPR];
+  __shared__ float lane_m[THREADS / 64], lane_w[THREADS / 64];
 
   const int tid = threadIdx.x;
   const int bh = blockIdx.x / SLICES;
@@ -73,45 +64,14 @@ __global__ __launch_bounds__(THREADS) void reduce_kernel(ReduceArgs a) {
   r1 = max(r0, min(r1, a.total_rows));
   const int nr = r1 - r0;
 
-  // M and W = sum_r 2^(lse2_r - M), each in a fixed order.
-  float mx = -INFINITY;
-  for (int r = tid; r < nr; r += THREADS)
-    mx = fmaxf(mx, a.partial_lse2[(int64_t)(r0 + r) * a.heads + h]);
-  mx = wave_max(mx);
-  if ((tid & 63) == 0) red[tid >> 6] = mx;
-  __syncthreads();
-  float M = red[0];
-#pragma unroll
-  for (int w = 1; w < THREADS / 64; ++w) M = fmaxf(M, red[w]);
-  __syncthreads();
-
   const int c4 = tid % TPR;    // which 4 dims of the slice
   const int rl = tid / TPR;    // which row lane
   const int d0 = slice * SLICE + c4 * 4;
   const int64_t oidx = ((int64_t)b * a.heads + h) * LAT + d0;
 
-  if (M == -INFINITY) {
-    // Nothing visible in any row: zeros and -inf, never NaN.
-    if (rl == 0) {
-      typename E::vec4 z;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) z[j] = static_cast<typename E::scalar>(0.0f);
-      *reinterpret_cast<typename E::vec4*>(reinterpret_cast<uint16_t*>(a.out) + oidx) = z;
-    }
-    if (a.lse2_out && slice == 0 && tid == 0) a.lse2_out[(int64_t)b * a.heads + h] = -INFINITY;
-    return;
-  }
-
-  float wsum = 0.f;
-  for (int r = tid; r < nr; r += THREADS)
-    wsum += __builtin_amdgcn_exp2f(a.partial_lse2[(int64_t)(r0 + r) * a.heads + h] - M);
-  wsum = wave_sum(wsum);
-  if ((tid & 63) == 0) red[tid >> 6] = wsum;
-  __syncthreads();
-  float W = red[0];
-#pragma unroll
-  for (int w = 1; w < THREADS / 64; ++w) W += red[w];
-
+  // Running merge of this row lane's rows: maximum m, sum of 2^(lse - m) O
+  // and of 2^(lse - m). Rows with lse2 = -inf (no visible token) weigh 0.
+  float m = -INFINITY, w = 0.f;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int rb = rl; rb < nr; rb += RL * UNROLL) {
     f32x4 v[UNROLL];
@@ -123,25 +83,76 @@ __global__ __launch_bounds__(THREADS) void reduce_kernel(ReduceArgs a) {
       lw[j] = a.partial_lse2[row * a.heads + h];
       v[j] = *reinterpret_cast<const f32x4*>(a.partial_out + (row * a.heads + h) * LAT + d0);
     }
+    float bm = m;
 #pragma unroll
-    for (int j = 0; j < UNROLL; ++j) {
-      if (rb + j * RL < nr) acc += __builtin_amdgcn_exp2f(lw[j] - M) * v[j];
+    for (int j = 0; j < UNROLL; ++j)
+      if (rb + j * RL < nr) bm = fmaxf(bm, lw[j]);
+    if (bm > m) {   // bm is finite here
+      const float alpha = __builtin_amdgcn_exp2f(m - bm);   // 0 when m = -inf
+      acc *= alpha;
+      w *= alpha;
+      m = bm;
+    }
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int j = 0; j < UNROLL; ++j) {
+        if (rb + j * RL < nr) {
+          const float e = __builtin_amdgcn_exp2f(lw[j] - m);
+          acc += e * v[j];
+          w += e;
+        }
+      }
     }
   }
-  part[rl][c4] = acc;
-  __syncthreads();
-  if (rl == 0) {
-    f32x4 tot = part[0][c4];
+  // Merge the row lanes: first the 8 of each wave through lane shuffles
+  // (lane bits 3..5), then the 4 waves through LDS, each in a fixed order.
+  auto merge = [&](float m2, float w2, f32x4 acc2) {
+    const float mn = fmaxf(m, m2);
+    const float s1 = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+    const float s2 = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
+    acc = s1 * acc + s2 * acc2;
+    w = s1 * w + s2 * w2;
+    m = mn;
+  };
 #pragma unroll
-    for (int k = 1; k < RL; ++k) tot += part[k][c4];
-    const float inv = 1.0f / W;
-    typename E::vec4 o;
+  for (int x = 8; x < 64; x <<= 1) {
+    f32x4 acc2;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = static_cast<typename E::scalar>(tot[j] * inv);
-    *reinterpret_cast<typename E::vec4*>(reinterpret_cast<uint16_t*>(a.out) + oidx) = o;
-    if (a.lse2_out && slice == 0 && c4 == 0)
-      a.lse2_out[(int64_t)b * a.heads + h] = M + __builtin_amdgcn_logf(W);
+    for (int j = 0; j < 4; ++j) acc2[j] = shfl_xor(acc[j], x);
+    merge(shfl_xor(m, x), shfl_xor(w, x), acc2);
   }
+  const int wv = tid >> 6;
+  if ((tid & 63) < TPR) {
+    part[wv][c4] = acc;
+    if (c4 == 0) {
+      lane_m[wv] = m;
+      lane_w[wv] = w;
+    }
+  }
+  __syncthreads();
+  if (tid >= TPR) return;
+  // Thread c4 of wave 0 (its own merged state is wave 0's entry).
+#pragma unroll
+  for (int k = 1; k < THREADS / 64; ++k) merge(lane_m[k], lane_w[k], part[k][c4]);
+  const float M = m;
+  if (M == -INFINITY) {
+    // Nothing visible in any row: zeros and -inf, never NaN.
+    typename E::vec4 z;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) z[j] = static_cast<typename E::scalar>(0.0f);
+    *reinterpret_cast<typename E::vec4*>(reinterpret_cast<uint16_t*>(a.out) + oidx) = z;
+    if (a.lse2_out && slice == 0 && c4 == 0) a.lse2_out[(int64_t)b * a.heads + h] = -INFINITY;
+    return;
+  }
+  const f32x4 tot = acc;
+  const float W = w;
+  const float inv = 1.0f / W;
+  typename E::vec4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = static_cast<typename E::scalar>(tot[j] * inv);
+  *reinterpret_cast<typename E::vec4*>(reinterpret_cast<uint16_t*>(a.out) + oidx) = o;
+  if (a.lse2_out && slice == 0 && c4 == 0)
+    a.lse2_out[(int64_t)b * a.heads + h] = M + __builtin_amdgcn_logf(W);
 }
 
 bool aligned(const void* p, uintptr_t k) { return (reinterpret_cast<uintptr_t>(p) % k) == 0; }

@@ -46,9 +46,9 @@ FETCH_SCALE = 2.0
 WRITE_SCALE = 1.0
 MEASURED = {
     # profiles/partition_kernel_v2lite_32k.md
-    ("v2lite_32k", "adfa15276ed6"): dict(fetch_kib=18627.3, write_kib=8208.0, mfma_busy=0.020),
+    ("v2lite_32k", "64a7607287cb"): dict(fetch_kib=18618.3, write_kib=8208.0, mfma_busy=0.021),
     # profiles/wide_kernel_v3_131k.md
-    ("v3_131k", "e549477f5fed"): dict(fetch_kib=74473.0, write_kib=32832.0, mfma_busy=0.267),
+    ("v3_131k", "bbdaee8b974d"): dict(fetch_kib=74482.3, write_kib=32832.0, mfma_busy=0.270),
 }
 
 
