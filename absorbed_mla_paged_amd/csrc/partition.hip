@@ -107,19 +107,6 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
   const int64_t qrow0 = (int64_t)b * a.heads + head0;   // first (b, head) row
   const int my_head = head0 + ln;
 
-  // Q (compute waves; its address needs no metadata). B operand of the
-  // score product: lane (ln, lg) holds head head0 + ln, dims 32 k + 8 lg ..
-  // + 8. Compute waves issue no copies, so the compiler's own wait for Q is
-  // exact.
-  vec8 q[KSTEPS];
-  if (!copier) {
-    const vec8* qa = reinterpret_cast<const vec8*>(a.q_absorbed + (qrow0 + ln) * LAT);
-    const vec8* qp = reinterpret_cast<const vec8*>(a.q_pe + (qrow0 + ln) * ROPE);
-#pragma unroll
-    for (int k = 0; k < KSTEPS; ++k)
-      q[k] = (k < LAT / 32) ? qa[4 * k + lg] : qp[4 * (k - LAT / 32) + lg];
-  }
-
   // All row metadata in one round trip.
   int n = load_const(context_lens, b);
   int P = 1, S = 1, row = b, nrows = 1;
@@ -160,6 +147,22 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
   if (tid < 6) ready[tid] = 0u;
   __syncthreads();
 
+  // Q (compute waves), loaded after the barrier: it is needed only once
+  // the first stage has landed, and its kernel-argument fetch and loads
+  // would otherwise hold the compute waves (and so the copy waves) at the
+  // barrier. B operand of the score product: lane (ln, lg) holds head
+  // head0 + ln, dims 32 k + 8 lg .. + 8. Compute waves issue no copies, so
+  // the compiler's own wait for Q is exact.
+  vec8 q[KSTEPS];
+  if (!copier) {
+    const vec8* qa = reinterpret_cast<const vec8*>(a.q_absorbed + (qrow0 + ln) * LAT);
+    const vec8* qp = reinterpret_cast<const vec8*>(a.q_pe + (qrow0 + ln) * ROPE);
+#pragma unroll
+    for (int k = 0; k < KSTEPS; ++k)
+      q[k] = (k < LAT / 32) ? qa[4 * k + lg] : qp[4 * (k - LAT / 32) + lg];
+  }
+
+
   if (nst <= 0) {
     // No visible token: zero output, lse2 = -inf.
     if (copier) return;
@@ -198,21 +201,28 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
     const char* ckv_base = reinterpret_cast<const char*>(a.ckv);
     const char* kpe_base = reinterpret_cast<const char*>(a.kpe);
     const uint32_t base = lds_addr(smem) + slot * STAGE;
+    // Physical blocks of stage k (a one-block stage copies its block twice,
+    // an L2 hit; its second half is never read). Looked up one stage
+    // ahead, so the block-table round trip overlaps the waits below.
+    auto lookup = [&](int k, int64_t* ph) {
+      const int nb_here = min(2, nblocks - 2 * k);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int blk = blk_lo + 2 * k + min(j, nb_here - 1);
+        const int v = __builtin_amdgcn_readfirstlane(load_const(block_table, tbl0 + blk));
+        ph[j] = (int64_t)max(0, min(v, last_blk));
+      }
+    };
+    int64_t phys[2], phys_next[2] = {0, 0};
+    if (slot < nst) lookup(slot, phys_next);
     for (int k = slot, g = 0; k < nst; k += 2, ++g) {
+      phys[0] = phys_next[0];
+      phys[1] = phys_next[1];
+      if (k + 2 < nst) lookup(k + 2, phys_next);
       wait_counter(freed + slot, CWAVES * g);
       // Stages are issued in order, so the memory queue returns them in
       // order and stage k can be computed while stage k + 1 is arriving.
       wait_counter(issued, 2 * k);
-      const int nb_here = min(2, nblocks - 2 * k);
-      int64_t phys[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        // A one-block stage copies its block twice (an L2 hit); its second
-        // half is never read.
-        const int blk = blk_lo + 2 * k + min(j, nb_here - 1);
-        const int v = __builtin_amdgcn_readfirstlane(load_const(block_table, tbl0 + blk));
-        phys[j] = (int64_t)max(0, min(v, last_blk));
-      }
       // ops 0..63: ckv rows (block op / 32, row op % 32); 64..71: kpe rows
       // 8 (op - 64) .. + 8 of the stage.
 #pragma unroll
