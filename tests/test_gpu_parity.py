@@ -187,6 +187,44 @@ def test_reduce_matches_oracle_merge_and_rejects_ln_lse():
             assert err > 10 * 1e-2
 
 
+@pytest.mark.parametrize("hot_tail", [False, True])
+def test_reduce_many_rows_online_merge(hot_tail):
+    # 600 rows for one request: each row lane of the reduce takes its rows in
+    # three batches of eight, keeping a running maximum. With the latent
+    # values of the last 16 blocks scaled up, the largest LSEs sit in the
+    # last rows, so the running sums are rescaled in the later batches. The
+    # first 40 rows are emptied (LSE -inf, zero partial): lanes start from a
+    # maximum of -inf.
+    import torch
+    case = small(131, [32768], 16, "f16")
+    if hot_tail:
+        blocks = case.block_table[0, 1024 - 16:1024]
+        hot = reference.decode16(case.ckv_pool[blocks], case.dtype) * 1.5
+        case.ckv_pool[blocks] = mla_synth.encode16(hot.astype(np.float32), case.dtype)
+    ranges = oracle.row_ranges(case.context_lens, [12], [50])
+    assert len(ranges) == 600
+    po, pl = oracle.partials_f64(case, ranges, [0, 600])
+    po[:40] = 0.0
+    pl[:40] = -np.inf
+    ref, lref = reference.merge_log2_f64(po, pl, [0, 600])
+    ind = torch.tensor([0, 600], dtype=torch.int32, device="cuda")
+    out = torch.empty((1, 16, 512), dtype=torch.float16, device="cuda")
+    lse = torch.empty((1, 16), dtype=torch.float32, device="cuda")
+    po_d = torch.tensor(po, dtype=torch.float32, device="cuda")
+    pl_d = torch.tensor(pl, dtype=torch.float32, device="cuda")
+    mla.mla_decode_reduce(po_d, pl_d, ind, 1, 16, 600, out, lse)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    err = np.abs(got - ref)
+    log(f"[reduce] 600 rows hot_tail={hot_tail}: max err {err.max():.3e} mean {err.mean():.3e}")
+    assert err.max() <= 1e-2 and err.mean() <= 1e-3
+    assert np.max(np.abs(lse.cpu().numpy() - lref)) < 1e-4
+    a = out.clone()
+    mla.mla_decode_reduce(po_d, pl_d, ind, 1, 16, 600, out, lse)
+    torch.cuda.synchronize()
+    assert torch.equal(a, out)
+
+
 def test_reduce_all_empty_rows_give_zero():
     import torch
     po = torch.zeros((3, 16, 512), dtype=torch.float32, device="cuda")
