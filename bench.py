@@ -46,7 +46,7 @@ FETCH_SCALE = 2.0
 WRITE_SCALE = 1.0
 MEASURED = {
     # profiles/partition_kernel_v2lite_32k.md
-    ("v2lite_32k", "64a7607287cb"): dict(fetch_kib=18618.3, write_kib=8208.0, mfma_busy=0.021),
+    ("v2lite_32k", "bbf9bede109c"): dict(fetch_kib=18626.3, write_kib=8208.0, mfma_busy=0.021),
     # profiles/wide_kernel_v3_131k.md
     ("v3_131k", "bbdaee8b974d"): dict(fetch_kib=74482.3, write_kib=32832.0, mfma_busy=0.270),
 }
@@ -59,6 +59,31 @@ def kernel_hash(hpw: int) -> str:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:12]
+
+
+def host_chooser_us(case, prm, calls: int = 2000) -> float:
+    """Host time of one mla_choose_partitions call (the plan of every step),
+    through ctypes with the arguments built once: an upper bound on the C
+    call itself."""
+    import ctypes
+    import absorbed_mla_paged_amd as mla
+    lib = mla.load_library()
+    B = case.batch
+    ctx = (ctypes.c_int32 * B)(*[int(n) for n in case.context_lens])
+    P = (ctypes.c_int32 * B)()
+    S = (ctypes.c_int32 * B)()
+    ind = (ctypes.c_int32 * (B + 1))()
+    info = mla._PlanInfo()
+    c_prm = prm._c() if prm is not None else None
+    pp = ctypes.byref(c_prm) if c_prm is not None else None
+    args = (B, case.heads, 1, ctx, 32, pp, P, S, ind, ctypes.byref(info))
+    fn = lib.mla_choose_partitions
+    if fn(*args) != 0:
+        raise RuntimeError(mla.mla_last_error())
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        fn(*args)
+    return (time.perf_counter() - t0) / calls * 1e6
 
 
 def log(*a):
@@ -199,9 +224,12 @@ def main():
     if not torch.equal(out, eager):
         log("[bench] timed replay differs from the eager result")
         sys.exit(3)
-    ms_per_step = gpu_ms / args.steps
+    device_ms = gpu_ms / args.steps
+    chooser_us = host_chooser_us(case, prm)
+    # The step is the whole path: the host chooser, then the device work.
+    ms_per_step = device_ms + chooser_us * 1e-3
     log(f"[bench] {args.steps} steps: {gpu_ms:.3f} ms GPU ({wall * 1e3:.3f} ms wall) "
-        f"-> {ms_per_step * 1e3:.2f} us/step")
+        f"-> {device_ms * 1e3:.2f} us/step on the device + {chooser_us:.2f} us host chooser")
 
     # Partition kernel alone: back-to-back launches (rotating copies) in a
     # graph, HIP events on the launch stream around them.
@@ -259,6 +287,8 @@ def main():
                    "block_size": 32, "kv_lora_rank": 512, "rope_dim": 64,
                    "plan": {"P": info["P"], "S": info["S"], "rows": info["total_rows"]},
                    "single_pass": bool(args.single_pass), "kv_copies": ncopy},
+        "device_us": round(device_ms * 1e3, 3),
+        "host_chooser_us": round(chooser_us, 3),
         "achieved_gbs_pair": round(pair_gbs, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
