@@ -257,6 +257,36 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
     }
   };
 
+  // Q of the workgroup's 64 heads (64 rows of 512 latent dims, then 64 rows
+  // of 64 rope dims: 72 KB) goes through LDS once, into ring slots 2 and 3,
+  // which stay idle until step 0; each of the 8 waves copies 9 KB of it.
+  // Loaded per score wave straight from memory it would cost every CU
+  // 144 KB (two waves share each head), twice the first two KV blocks.
+  // Rows are swizzled like the KV rows.
+  const uint32_t qlds = lds0 + 2 * SLOT;
+  static_assert(HPW * (CKV_ROW + KPE_ROW) == 2 * SLOT && 8 * OPW == HPW + HPW * KPE_ROW / 1024,
+                "Q staging fills slots 2 and 3 in 8 x 9 copies");
+  auto issue_q = [&]() {
+    const int64_t q0 = (int64_t)b * a.heads + hwg;
+    const char* qa_base = reinterpret_cast<const char*>(a.q_absorbed + q0 * LAT);
+    const char* qp_base = reinterpret_cast<const char*>(a.q_pe + q0 * ROPE);
+    int lane;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(lane) : "v"(lane_id));
+#pragma unroll
+    for (int i = 0; i < OPW; ++i) {
+      const int op = wave * OPW + i;   // 0..63 latent rows, 64..71 rope rows 8 (op - 64) .. + 8
+      if (op < HPW) {
+        const uint32_t voff = ((lane & ~15) | ((lane & 15) ^ swz_ckv(op))) * 16;
+        dma16s(voff, qa_base + op * CKV_ROW, qlds + op * CKV_ROW);
+      } else {
+        const int t8 = op - HPW;
+        const int r = t8 * 8 + (lane >> 3);
+        const uint32_t voff = (lane >> 3) * KPE_ROW + ((lane & 7) ^ swz_kpe(r)) * 16;
+        dma16s(voff, qp_base + t8 * 1024, qlds + HPW * CKV_ROW + t8 * 1024);
+      }
+    }
+  };
+
   MLA_LDS float* xm = (MLA_LDS float*)(smem + XM);   // [score wave][j][ln]
   MLA_LDS uint32_t* flag = (MLA_LDS uint32_t*)(smem + XFLAG);
   if (tid == 0) *flag = 0u;   // seen by all after the first meeting below
@@ -267,41 +297,49 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
   // The two roles run separate copies of the pass / step loops (so Q and
   // the accumulators are never live in the same wave) that meet at the same
   // barriers in the same order:
+  //   before step 0:   M_q (Q is in LDS)
   //   per step i:      M_step(i)  [+ M_ref in step 0 of the first pass]
   //   after a pass:    M_flag     [+ M_x1, M_x2 before a second pass]
   //   epilogue:        M_epi
   if (scorer) {
     // Q: lane (ln, lg) of head tile j holds head hwg + 32 hp + 16 j + ln,
-    // dims 32 k + 8 lg .. + 8. With two waves per SIMD the compiler gives
-    // each wave 128 VGPRs and 128 AGPRs, and it puts every MFMA accumulator
-    // in AGPRs (here the four score chains, 16 registers). The first KA
-    // K-steps of Q (112 registers) are loaded straight into AGPRs, which the
-    // score MFMAs read as their B operand; the rest go to VGPRs. The AGPR
-    // loads are ours, not the compiler's, so they are waited for explicitly
-    // (before any copy is issued).
+    // dims 32 k + 8 lg .. + 8, read from the LDS copy of Q. With two waves
+    // per SIMD the compiler gives each wave 128 VGPRs and 128 AGPRs, and it
+    // puts every MFMA accumulator in AGPRs (here the four score chains, 16
+    // registers). The first KA K-steps of Q (112 registers) are read
+    // straight into AGPRs, which the score MFMAs use as their B operand; the
+    // rest go to VGPRs.
+    issue_q();
+    wait_vmcnt<0>();
+    meet();   // M_q: Q is in LDS
     constexpr int KA = 14;
     u32x4 q[2][KA];
     vec8 qv[2][KSTEPS - KA];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int64_t qr = (int64_t)b * a.heads + hwg + 32 * hp + 16 * j + ln;
-      const u32x4* qa = reinterpret_cast<const u32x4*>(a.q_absorbed + qr * LAT);
-      const vec8* qav = reinterpret_cast<const vec8*>(a.q_absorbed + qr * LAT);
-      const vec8* qp = reinterpret_cast<const vec8*>(a.q_pe + qr * ROPE);
+      const int r = 32 * hp + 16 * j + ln;
 #pragma unroll
-      for (int k = 0; k < KA; ++k)
-        asm volatile("global_load_dwordx4 %0, %1, off" : "=a"(q[j][k]) : "v"(qa + 4 * k + lg) : "memory");
-#pragma unroll
-      for (int k = KA; k < KSTEPS; ++k)
-        qv[j][k - KA] = (k < LAT / 32) ? qav[4 * k + lg] : qp[4 * (k - LAT / 32) + lg];
+      for (int k = 0; k < KSTEPS; ++k) {
+        const uint32_t addr =
+            k < LAT / 32 ? qlds + r * CKV_ROW + (((4 * k + lg) ^ swz_ckv(r)) * 16)
+                         : qlds + HPW * CKV_ROW + r * KPE_ROW +
+                               (((4 * (k - LAT / 32) + lg) ^ swz_kpe(r)) * 16);
+        if (k < KA)
+          asm volatile("ds_read_b128 %0, %1" : "=a"(q[j][k]) : "v"(addr) : "memory");
+        else
+          qv[j][k - KA] = lds_read_b128<vec8>(addr);
+      }
     }
-    wait_vmcnt<0>();
-    // Tie the AGPR halves of Q to that wait (the compiler does not know the
-    // asm loads are asynchronous; a use is safe only after an ordered asm).
+    // The reads are asynchronous to the compiler: wait, then tie every value
+    // to that wait (a use is safe only after an ordered asm statement).
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j) {
 #pragma unroll
       for (int k = 0; k < KA; ++k) asm volatile("" : "+a"(q[j][k]));
+#pragma unroll
+      for (int k = 0; k < KSTEPS - KA; ++k) asm volatile("" : "+v"(qv[j][k]));
+    }
     auto qfrag = [&](int j, int ks) {
       return ks < KA ? __builtin_bit_cast(vec8, q[j][ks < KA ? ks : 0])
                      : qv[j][ks < KA ? 0 : ks - KA];
@@ -498,6 +536,7 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
       __builtin_amdgcn_sched_barrier(0);   // as in the score loop
     }
   };
+  issue_q();
   for (int pass = 0; pass < 2; ++pass) {
     // Blocks 0 and 1 before the first step (the rest during the steps).
     const int npro = min(NPRO, nblocks);
@@ -505,6 +544,10 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
       const int64_t ph = phys_of(k);
 #pragma unroll
       for (int c = 0; c < OPW; ++c) issue_one(k, ph, c);
+    }
+    if (pass == 0) {
+      wait_blocks(npro);   // my part of Q has landed (the block copies may not have)
+      meet();              // M_q
     }
     // Start of step i: block i must be in LDS (my later copies, of blocks
     // i + 1 .. last, may still be in flight), then M_step(i), then the copy
