@@ -48,7 +48,7 @@ MEASURED = {
     # profiles/partition_kernel_v2lite_32k.md
     ("v2lite_32k", "bbf9bede109c"): dict(fetch_kib=18626.3, write_kib=8208.0, mfma_busy=0.021),
     # profiles/wide_kernel_v3_131k.md
-    ("v3_131k", "bbdaee8b974d"): dict(fetch_kib=74482.3, write_kib=32832.0, mfma_busy=0.270),
+    ("v3_131k", "94716a332236"): dict(fetch_kib=74492.8, write_kib=32832.0, mfma_busy=0.283),
 }
 
 
