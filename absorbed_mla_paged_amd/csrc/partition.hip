@@ -38,6 +38,12 @@
 //  * Values: O^T[dim, head] += V^T[dim, token] . P^T[token, head] on
 //    v_mfma_f32_16x16x32; V^T is read from the same LDS tile with
 //    ds_read_b64_tr_b16. Compute wave w owns dims [128 w, 128 w + 128).
+//  * LDS fragment reads in both MFMA loops are issued ahead from inline asm
+//    (dev::lds_read_*) with explicit lgkmcnt waits; a wait names every
+//    register it guards.
+//  * Outputs go out as device-scope write-through buffer stores, so the
+//    release at the end of the kernel has no dirty partial lines left to
+//    write back before the reduce can start.
 #include "partition_common.h"
 
 #include <cmath>
