@@ -11,8 +11,8 @@
 // its log2-sum-exp, or rounded into `out` for a single-row request.
 //
 // With 64 heads the arithmetic per cached byte is high enough that the
-// matrix cores and LDS, not HBM, set the pace, so the layout keeps each
-// SIMD's MFMA pipe fed from two waves with different jobs:
+// matrix cores and LDS are about as busy as the memory path, so the layout
+// keeps each SIMD's MFMA pipe fed from two waves with different jobs:
 //  * 512 threads = 8 wave64, two per SIMD (256 registers each). Waves 0-3
 //    score, waves 4-7 apply values. The big per-wave arrays live in AGPRs:
 //    Q (the score MFMAs' B operand) in score waves, the accumulators in
@@ -32,10 +32,12 @@
 //    waves apply block i - 1 (probabilities double-buffered by parity); one
 //    s_barrier per step. LDS holds a ring of 4 one-block slots (32 KB ckv +
 //    4 KB kpe), filled by the value waves with global_load_lds_dwordx4 (16 B
-//    per lane, a quarter of each block per wave): blocks 0 and 1 while the
-//    score waves load Q, then block i + 2 right after the meeting of step i,
-//    into the slot of block i - 2 that the meeting has just freed. Each
-//    block thus has two steps to arrive.
+//    per lane, a quarter of each block per wave): blocks 0 and 1 before the
+//    first step, then block i + 2 right after the meeting of step i, into
+//    the slot of block i - 2 that the meeting has just freed. Each block
+//    thus has two steps to arrive; that lead, not the arithmetic, bounds the
+//    kernel. Before step 0 all waves stage the workgroup's Q through slots 2
+//    and 3, and the score waves read their fragments from there.
 //  * No rescaling inside the loop: every head's reference maximum is the
 //    maximum over the row's first block, and probabilities relative to it
 //    may grow up to 2^15 (finite in fp16 and bf16, exact to the format's
@@ -44,7 +46,9 @@
 //    workgroup makes a second pass over the row with the exact maxima as
 //    references. The accumulators only ever see MFMA updates.
 //  * LDS fragment reads in the MFMA loops are issued several MFMAs ahead
-//    (dev::lds_read_*), with explicit lgkmcnt waits.
+//    (dev::lds_read_*), with explicit lgkmcnt waits that name every register
+//    they guard.
+//  * Partials go out as device-scope write-through buffer stores.
 #include "partition_common.h"
 
 #include <cmath>
