@@ -18,13 +18,14 @@ LIB_PATH = os.path.join(HERE, "libmla_decode.so")
 
 MLA_F16, MLA_BF16 = 0, 1
 KV_LORA_RANK, ROPE_DIM, BLOCK_SIZE = 512, 64, 32
+FUSED_SYNC_BYTES_PER_REQUEST = 512
 STATUS = {0: "MLA_OK", -1: "MLA_E_NULL", -2: "MLA_E_SHAPE", -3: "MLA_E_RANGE",
           -4: "MLA_E_ALIGN", -5: "MLA_E_WORKSPACE", -6: "MLA_E_UNSUPPORTED",
           -7: "MLA_E_HIP"}
 
 # Every function include/mla_decode.h declares.
 EXPORTS = ["mla_default_plan_params", "mla_choose_partitions", "mla_partition_range",
-           "mla_decode_partition", "mla_decode_reduce", "mla_status_string",
+           "mla_decode_partition", "mla_decode_reduce", "mla_decode_fused", "mla_status_string",
            "mla_last_error", "mla_get_counters", "mla_reset_counters"]
 
 
@@ -81,6 +82,10 @@ def load_library(path: str | None = None):
     lib.mla_decode_partition.restype = ctypes.c_int
     lib.mla_decode_reduce.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
     lib.mla_decode_reduce.restype = ctypes.c_int
+    lib.mla_decode_fused.argtypes = [vp, vp, vp, vp, i32, vp, i32, vp, i32, i32,
+                                     ctypes.c_float, i32, vp, vp, vp, i32, i32, i32,
+                                     vp, vp, vp, vp, vp, vp, vp]
+    lib.mla_decode_fused.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_last_error.argtypes = []
@@ -220,6 +225,23 @@ def mla_decode_partition(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, co
         _ptr(partial_lse2), _ptr(out), _ptr(lse2_out), _ptr(debug_ranges), _stream(stream)))
 
 
+def mla_decode_fused(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens,
+                     scale: float, partitions, splits, row_indptr, total_rows: int,
+                     max_rows_per_req: int, heads_per_wg: int, partial_out, partial_lse2,
+                     out, lse2_out, sync, debug_ranges=None, stream=None):
+    """Partition and merge in one launch (see include/mla_decode.h)."""
+    lib = load_library()
+    _need_cuda(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens, out)
+    B, H = int(q_absorbed.shape[0]), int(q_absorbed.shape[1])
+    _check(lib.mla_decode_fused(
+        _ptr(q_absorbed), _ptr(q_pe), _ptr(ckv_cache), _ptr(kpe_cache), int(ckv_cache.shape[0]),
+        _ptr(block_table), int(block_table.shape[1]), _ptr(context_lens), B, H,
+        float(scale), _dtype_code(q_absorbed), _ptr(partitions), _ptr(splits), _ptr(row_indptr),
+        int(total_rows), int(max_rows_per_req), int(heads_per_wg), _ptr(partial_out),
+        _ptr(partial_lse2), _ptr(out), _ptr(lse2_out), _ptr(sync), _ptr(debug_ranges),
+        _stream(stream)))
+
+
 def mla_decode_reduce(partial_out, partial_lse2, row_indptr, batch: int, num_heads: int,
                       total_rows: int, out, lse2_out=None, stream=None):
     """Launch the LSE-weighted reduce (see include/mla_decode.h)."""
@@ -251,6 +273,10 @@ class DecodePlan:
             self.partial_lse2 = torch.empty((rows, num_heads), dtype=torch.float32, device=device)
         else:
             self.partial_out = self.partial_lse2 = None
+        # Hand-off state of the fused launch: zero-filled once, left ready
+        # by every completed call.
+        self.sync = torch.zeros(max(1, self.batch) * FUSED_SYNC_BYTES_PER_REQUEST // 8,
+                                dtype=torch.int64, device=device)
 
     @property
     def total_rows(self) -> int:
@@ -258,8 +284,16 @@ class DecodePlan:
 
 
 def decode(plan: DecodePlan, q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens,
-           scale: float, out, lse2_out=None, debug_ranges=None, stream=None):
-    """Partition launch, then the reduce launch when the plan needs one."""
+           scale: float, out, lse2_out=None, debug_ranges=None, stream=None, fused=False):
+    """Partition launch, then the reduce launch when the plan needs one; with
+    fused=True, one launch that merges too."""
+    if fused:
+        mla_decode_fused(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens, scale,
+                         plan.partitions, plan.splits, plan.row_indptr, plan.total_rows,
+                         plan.info["max_rows_per_req"], plan.info["heads_per_wg"],
+                         plan.partial_out, plan.partial_lse2, out, lse2_out, plan.sync,
+                         debug_ranges, stream)
+        return
     mla_decode_partition(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens, scale,
                          plan.partitions, plan.splits, plan.row_indptr, plan.total_rows,
                          plan.info["max_rows_per_req"], plan.info["heads_per_wg"],

@@ -44,6 +44,7 @@
 //  * Outputs go out as device-scope write-through buffer stores, so the
 //    release at the end of the kernel has no dirty partial lines left to
 //    write back before the reduce can start.
+#include "fused_common.h"
 #include "partition_common.h"
 
 #include <cmath>
@@ -75,7 +76,7 @@ static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 // The leading scalar kernel arguments (16 dwords, up to block_table) are
 // preloaded into SGPRs at wave launch on gfx950, so finding the row costs
 // no argument fetch; the PartitionArgs block is fetched meanwhile.
-template <int DT>
+template <int DT, bool FUSED>
 __global__ __launch_bounds__(THREADS) void partition_kernel(
     int32_t groups, int32_t rows_per_req, int32_t slots, int32_t direct, int32_t total_rows,
     int32_t max_blocks, const int32_t* __restrict__ context_lens,
@@ -113,6 +114,17 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
   const int64_t qrow0 = (int64_t)b * a.heads + head0;   // first (b, head) row
   const int my_head = head0 + ln;
 
+  // Fused launches: the bases of the merge hand-off state, read first.
+  uint64_t* fh = nullptr;
+  uint64_t f_sbase = 0, f_abase = 0, f_seen = 0;
+  if constexpr (FUSED) {
+    fh = fused::header(a.sync, b, hg);
+    if (tid == 0) {
+      f_sbase = fused::ld(fh + fused::kSbase);
+      f_abase = fused::ld(fh + fused::kAbase);
+    }
+  }
+
   // All row metadata in one round trip.
   int n = load_const(context_lens, b);
   int P = 1, S = 1, row = b, nrows = 1;
@@ -128,6 +140,10 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
   }
   n = max(0, min(n, max_blocks * BS));
   if (x >= nrows || row < 0 || row >= total_rows) return;
+  if constexpr (FUSED) {
+    if (tid == 0)
+      __hip_atomic_fetch_add(fh + fused::kStarted, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   const int p = x / S;
   const int s = x % S;
   // Index math of mla_partition_range (must agree bit for bit).
@@ -150,8 +166,34 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
   MLA_LDS uint32_t* freed = ready + 2;
   MLA_LDS uint32_t* issued = ready + 4;
   MLA_LDS uint32_t* scored = ready + 5;  // compute waves: score tiles written
-  if (tid < 6) ready[tid] = 0u;
+  MLA_LDS uint32_t* stored = ready + 6;  // compute waves: outputs stored (fused)
+  MLA_LDS uint32_t* decided = ready + 7; // merge pieces known (fused)
+  MLA_LDS int32_t* pieces = (MLA_LDS int32_t*)(ready + 8);   // first, count
+  if (tid < 8) ready[tid] = 0u;
   __syncthreads();
+
+  // Fused launches, every wave at its end (compute waves once their stores
+  // are issued): hand this row over, then merge the pieces it is given,
+  // reusing stage slot 0 of the LDS for the merge's exchange.
+  auto tail = [&]() {
+    if (!copier) {
+      wait_vmcnt<0>();   // this wave's stores have completed
+      bump_counter(stored, lane);
+      if (tid == 0) {
+        wait_counter(stored, CWAVES);
+        const fused::Decision d = fused::arrive(fh, f_sbase, f_abase, f_seen, nrows);
+        pieces[0] = d.first;
+        pieces[1] = d.count;
+        bump_counter(decided, lane);
+      }
+    }
+    wait_counter(decided, 1);
+    const int first = __builtin_amdgcn_readfirstlane(pieces[0]);
+    const int count = __builtin_amdgcn_readfirstlane(pieces[1]);
+    const fused::MergeArgs ma{a.partial_out, a.partial_lse2, a.out, a.lse2_out, a.heads};
+    for (int i = 0; i < count; ++i)
+      fused::merge_piece<DT, THREADS>(ma, first + i, nrows, (int64_t)(row - x), b, head0, HG, smem);
+  };
 
   // Q (compute waves), loaded after the barrier: it is needed only once
   // the first stage has landed, and its kernel-argument fetch and loads
@@ -171,7 +213,13 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
 
   if (nst <= 0) {
     // No visible token: zero output, lse2 = -inf.
-    if (copier) return;
+    if (copier) {
+      if constexpr (FUSED) tail();
+      return;
+    }
+    if constexpr (FUSED) {
+      if (tid == 0) f_seen = fused::ld(fh + fused::kStarted);
+    }
 #pragma unroll
     for (int dt = 0; dt < DT_PER_WAVE; ++dt) {
       const int d0 = (wave * DT_PER_WAVE + dt) * 16 + lg * 4;
@@ -194,6 +242,7 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
       a.debug_ranges[2 * row] = tok_lo;
       a.debug_ranges[2 * row + 1] = tok_hi;
     }
+    if constexpr (FUSED) tail();
     return;
   }
 
@@ -266,6 +315,7 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
       }
       bump_counter(ready + slot, lane);
     }
+    if constexpr (FUSED) tail();
     return;
   }
 
@@ -448,11 +498,17 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
     else values(std::integral_constant<int, DT_PER_WAVE>{});
     bump_counter(freed + slot, lane);
   }
+  if constexpr (FUSED) {
+    // All N workgroups of the request have begun by now unless the launch
+    // did not fit the device at once.
+    if (tid == 0) f_seen = fused::ld(fh + fused::kStarted);
+  }
   finish();
   if (a.debug_ranges && hg == 0 && tid == 0) {
     a.debug_ranges[2 * row] = tok_lo;
     a.debug_ranges[2 * row + 1] = tok_hi;
   }
+  if constexpr (FUSED) tail();
 }
 
 bool aligned(const void* p, uintptr_t k) { return (reinterpret_cast<uintptr_t>(p) % k) == 0; }
@@ -473,14 +529,17 @@ int device_compute_units(int64_t* cus) {
 
 using namespace mla;
 
-extern "C" int mla_decode_partition(
-    const void* q_absorbed, const void* q_pe, const void* ckv_cache, const void* kpe_cache,
-    int32_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
-    const int32_t* context_lens, int32_t batch, int32_t num_heads, float scale, int32_t dtype,
-    const int32_t* partitions, const int32_t* splits, const int32_t* row_indptr,
-    int32_t total_rows, int32_t max_rows_per_req, int32_t heads_per_wg, float* partial_out,
-    float* partial_lse2, void* out, float* lse2_out, int32_t* debug_ranges,
-    hipStream_t stream) {
+namespace {
+
+// Checks and launch shared by mla_decode_partition and mla_decode_fused.
+int partition_launch(bool fused, const void* q_absorbed, const void* q_pe, const void* ckv_cache,
+                     const void* kpe_cache, int32_t num_blocks, const int32_t* block_table,
+                     int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch,
+                     int32_t num_heads, float scale, int32_t dtype, const int32_t* partitions,
+                     const int32_t* splits, const int32_t* row_indptr, int32_t total_rows,
+                     int32_t max_rows_per_req, int32_t heads_per_wg, float* partial_out,
+                     float* partial_lse2, void* out, float* lse2_out, uint64_t* sync,
+                     int32_t* debug_ranges, hipStream_t stream) {
   clear_error();
   if (batch < 0) return fail(MLA_E_SHAPE, "batch %d < 0", batch);
   if (num_heads < MLA_MIN_HEADS || num_heads > MLA_MAX_HEADS || num_heads % 16)
@@ -511,6 +570,11 @@ extern "C" int mla_decode_partition(
       return fail(MLA_E_NULL, "split plan needs plan arrays and partial buffers");
     if (!aligned(partial_out, 16) || !aligned(partial_lse2, 4))
       return fail(MLA_E_ALIGN, "partial buffers misaligned");
+    if (fused) {
+      if (!out || !sync) return fail(MLA_E_NULL, "fused split plan needs `out` and `sync`");
+      if (!aligned(out, 16) || !aligned(sync, 64))
+        return fail(MLA_E_ALIGN, "out (16 bytes) or sync (64 bytes) misaligned");
+    }
   }
   if (!aligned(q_absorbed, 16) || !aligned(q_pe, 16) || !aligned(ckv_cache, 16) ||
       !aligned(kpe_cache, 16))
@@ -518,6 +582,9 @@ extern "C" int mla_decode_partition(
   if (!aligned(block_table, 4) || !aligned(context_lens, 4) || (lse2_out && !aligned(lse2_out, 4)) ||
       (debug_ranges && !aligned(debug_ranges, 8)))
     return fail(MLA_E_ALIGN, "int32/fp32 arrays misaligned");
+  const bool merge_here = fused && !direct;
+  if (merge_here && hpw != HG)
+    return fail(MLA_E_UNSUPPORTED, "fused merge with %d heads per workgroup", hpw);
 
   part::PartitionArgs a;
   a.q_absorbed = static_cast<const uint16_t*>(q_absorbed);
@@ -529,6 +596,7 @@ extern "C" int mla_decode_partition(
   a.out = out;
   a.lse2_out = lse2_out;
   a.debug_ranges = debug_ranges;
+  a.sync = merge_here ? sync : nullptr;
   a.num_blocks = num_blocks;
   a.heads = num_heads;
   a.scale_log2 = scale * 1.4426950408889634f;
@@ -539,21 +607,56 @@ extern "C" int mla_decode_partition(
   const int64_t wgs = ((slots + 7) / 8) * 8 * groups;
   if (wgs > INT32_MAX || slots > INT32_MAX)
     return fail(MLA_E_SHAPE, "grid too large (%lld workgroups)", (long long)wgs);
+  const dim3 grid((unsigned)wgs), block(THREADS);
+  const int32_t dflag = direct ? 1 : 0, sl = (int32_t)slots;
   if (hpw != HG)
-    part::launch_wide(dtype, hpw, (unsigned)wgs, stream, groups, rows_per_req, (int32_t)slots,
-                      direct ? 1 : 0, total_rows, max_blocks_per_seq, context_lens, row_indptr,
-                      partitions, splits, block_table, a);
-  else if (dtype == MLA_F16)
-    hipLaunchKernelGGL(partition_kernel<0>, dim3((unsigned)wgs), dim3(THREADS), 0, stream, groups,
-                       rows_per_req, (int32_t)slots, direct ? 1 : 0, total_rows, max_blocks_per_seq,
-                       context_lens, row_indptr, partitions, splits, block_table, a);
-  else
-    hipLaunchKernelGGL(partition_kernel<1>, dim3((unsigned)wgs), dim3(THREADS), 0, stream, groups,
-                       rows_per_req, (int32_t)slots, direct ? 1 : 0, total_rows, max_blocks_per_seq,
-                       context_lens, row_indptr, partitions, splits, block_table, a);
+    part::launch_wide(dtype, hpw, (unsigned)wgs, stream, groups, rows_per_req, sl, dflag,
+                      total_rows, max_blocks_per_seq, context_lens, row_indptr, partitions,
+                      splits, block_table, a);
+#define MLA_LAUNCH(K)                                                                        \
+  hipLaunchKernelGGL(K, grid, block, 0, stream, groups, rows_per_req, sl, dflag, total_rows, \
+                     max_blocks_per_seq, context_lens, row_indptr, partitions, splits,       \
+                     block_table, a)
+  else if (dtype == MLA_F16 && merge_here) MLA_LAUNCH((partition_kernel<0, true>));
+  else if (dtype == MLA_F16) MLA_LAUNCH((partition_kernel<0, false>));
+  else if (merge_here) MLA_LAUNCH((partition_kernel<1, true>));
+  else MLA_LAUNCH((partition_kernel<1, false>));
+#undef MLA_LAUNCH
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(MLA_E_HIP, "partition launch: %s", hipGetErrorString(e));
   count(direct ? 0 : 1, 1);
   count(3, (uint64_t)total_rows);
   return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" int mla_decode_partition(
+    const void* q_absorbed, const void* q_pe, const void* ckv_cache, const void* kpe_cache,
+    int32_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t batch, int32_t num_heads, float scale, int32_t dtype,
+    const int32_t* partitions, const int32_t* splits, const int32_t* row_indptr,
+    int32_t total_rows, int32_t max_rows_per_req, int32_t heads_per_wg, float* partial_out,
+    float* partial_lse2, void* out, float* lse2_out, int32_t* debug_ranges,
+    hipStream_t stream) {
+  return partition_launch(false, q_absorbed, q_pe, ckv_cache, kpe_cache, num_blocks, block_table,
+                          max_blocks_per_seq, context_lens, batch, num_heads, scale, dtype,
+                          partitions, splits, row_indptr, total_rows, max_rows_per_req,
+                          heads_per_wg, partial_out, partial_lse2, out, lse2_out, nullptr,
+                          debug_ranges, stream);
+}
+
+extern "C" int mla_decode_fused(
+    const void* q_absorbed, const void* q_pe, const void* ckv_cache, const void* kpe_cache,
+    int32_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t batch, int32_t num_heads, float scale, int32_t dtype,
+    const int32_t* partitions, const int32_t* splits, const int32_t* row_indptr,
+    int32_t total_rows, int32_t max_rows_per_req, int32_t heads_per_wg, float* partial_out,
+    float* partial_lse2, void* out, float* lse2_out, uint64_t* sync, int32_t* debug_ranges,
+    hipStream_t stream) {
+  return partition_launch(true, q_absorbed, q_pe, ckv_cache, kpe_cache, num_blocks, block_table,
+                          max_blocks_per_seq, context_lens, batch, num_heads, scale, dtype,
+                          partitions, splits, row_indptr, total_rows, max_rows_per_req,
+                          heads_per_wg, partial_out, partial_lse2, out, lse2_out, sync,
+                          debug_ranges, stream);
 }

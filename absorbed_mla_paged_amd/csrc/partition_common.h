@@ -21,6 +21,7 @@ struct PartitionArgs {
   void* out;
   float* lse2_out;
   int32_t* debug_ranges;
+  uint64_t* sync;    // merge hand-off state (fused launches only)
   int32_t num_blocks;
   int32_t heads;
   float scale_log2;  // scale * log2(e)

@@ -58,8 +58,10 @@ __global__ __launch_bounds__(THREADS) void reduce_kernel(ReduceArgs a) {
   const int b = bh / a.heads;
   const int h = bh % a.heads;
   if (b >= a.batch) return;
-  int r0 = a.row_indptr[b];
-  int r1 = a.row_indptr[b + 1];
+  // row_indptr[0] = 0 and row_indptr[batch] = total_rows by contract, so a
+  // single request needs no load before its partials.
+  int r0 = b == 0 ? 0 : a.row_indptr[b];
+  int r1 = b == a.batch - 1 ? a.total_rows : a.row_indptr[b + 1];
   r0 = max(0, min(r0, a.total_rows));
   r1 = max(r0, min(r1, a.total_rows));
   const int nr = r1 - r0;

@@ -34,7 +34,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "absorbed_mla_paged_amd", "csrc")
 # Sources of each partition kernel; their hash keys the counter table below.
 KERNEL_SOURCES = {
-    16: ["partition.hip", "partition_common.h", "device_common.h"],
+    16: ["partition.hip", "partition_common.h", "device_common.h", "fused_common.h"],
     64: ["partition_wide.hip", "partition_common.h", "device_common.h"],
 }
 # HBM traffic per partition launch from rocprofv3 --pmc (FETCH_SIZE and
@@ -133,6 +133,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="v2lite_32k")
     ap.add_argument("--single-pass", action="store_true", help="force P = S = 1")
+    ap.add_argument("--fused", action="store_true",
+                    help="partition and merge in one launch (mla_decode_fused)")
     ap.add_argument("--cold-bytes", type=float, default=1.5e9,
                     help="bytes of distinct KV copies cycled through (MALL is 256 MB)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -192,7 +194,7 @@ def main():
         # already hold its answer), then the device work.
         mla.mla_choose_partitions(case.batch, case.heads, 1, case.context_lens, prm)
         c, k = copies[j % ncopy]
-        mla.decode(plan, qa, qp, c, k, table, ctx, case.scale, out, lse2)
+        mla.decode(plan, qa, qp, c, k, table, ctx, case.scale, out, lse2, fused=args.fused)
 
     stream = torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()

@@ -52,6 +52,9 @@ extern "C" {
 #define MLA_MAX_SPLITS 4096
 #define MLA_MIN_HEADS 16
 #define MLA_MAX_HEADS 128
+/* Bytes of mla_decode_fused's hand-off state per request (8 head groups of
+ * 8 counters). */
+#define MLA_FUSED_SYNC_BYTES_PER_REQUEST 512
 
 typedef enum { MLA_F16 = 0, MLA_BF16 = 1 } mla_dtype;
 
@@ -234,6 +237,44 @@ int mla_decode_reduce(const float* partial_out, const float* partial_lse2,
                       const int32_t* row_indptr, int32_t batch, int32_t num_heads,
                       int32_t total_rows, int32_t dtype, void* out, float* lse2_out,
                       hipStream_t stream);
+
+/*
+ * mla_decode_fused -- partition and merge in one launch.
+ *
+ * The same result as mla_decode_partition followed by mla_decode_reduce,
+ * without the second launch and the gap between the two (the aim of the
+ * pages' direct write of partition 0 into the output: vllm-metal pull
+ * request 601, "What changed"). The workgroups of the launch write their
+ * fp32 partials as before; once every row of a request has arrived, the
+ * merge of that request (the reduce's log2-LSE merge, rounded once) is
+ * shared out among them and written to `out` and `lse2_out`. A workgroup
+ * only waits for the others when all of them have begun, so the launch
+ * finishes whether or not it fits the device at once (it is slower when it
+ * does not). A single-pass plan (total_rows == batch) is the same launch as
+ * mla_decode_partition.
+ *
+ * Arguments as mla_decode_partition, plus:
+ * out         dev 16-bit [batch, num_heads, 512], 16-byte aligned (always)
+ * lse2_out    dev fp32 [batch, num_heads] or NULL
+ * sync        dev, MLA_FUSED_SYNC_BYTES_PER_REQUEST * batch bytes, 64-byte
+ *             aligned, zero-filled before its first use. Every completed
+ *             call leaves it ready for the next one; calls that use the
+ *             same sync buffer must not run concurrently, and after a
+ *             launch that did not complete it must be zero-filled again.
+ *             Word 4 of each 64-byte record counts waits that ran out
+ *             (0 in correct use).
+ * Currently heads_per_wg must be 16 for split plans (MLA_E_UNSUPPORTED
+ * otherwise).
+ * Errors: as mla_decode_partition.
+ */
+int mla_decode_fused(const void* q_absorbed, const void* q_pe, const void* ckv_cache,
+                     const void* kpe_cache, int32_t num_blocks, const int32_t* block_table,
+                     int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch,
+                     int32_t num_heads, float scale, int32_t dtype, const int32_t* partitions,
+                     const int32_t* splits, const int32_t* row_indptr, int32_t total_rows,
+                     int32_t max_rows_per_req, int32_t heads_per_wg, float* partial_out,
+                     float* partial_lse2, void* out, float* lse2_out, uint64_t* sync,
+                     int32_t* debug_ranges, hipStream_t stream);
 
 /* Text for a status code (static storage). */
 const char* mla_status_string(int status);

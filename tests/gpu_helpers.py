@@ -41,7 +41,8 @@ def to_device(case, device="cuda"):
         context_lens=torch.from_numpy(np.ascontiguousarray(case.context_lens)).to(device))
 
 
-def run_case(case, params: mla.PlanParams | None = None, dev=None, want_ranges=False):
+def run_case(case, params: mla.PlanParams | None = None, dev=None, want_ranges=False,
+             fused=False):
     """Plan on the host, decode on the GPU; returns (out f64, lse2 f64, plan, ranges)."""
     import torch
     dev = dev or to_device(case)
@@ -53,7 +54,7 @@ def run_case(case, params: mla.PlanParams | None = None, dev=None, want_ranges=F
         ranges = torch.full((max(1, plan.total_rows), 2), -7, dtype=torch.int32, device="cuda")
     mla.decode(plan, dev["q_absorbed"], dev["q_pe"], dev["ckv_cache"], dev["kpe_cache"],
                dev["block_table"], dev["context_lens"], case.scale, out, lse2,
-               debug_ranges=ranges)
+               debug_ranges=ranges, fused=fused)
     torch.cuda.synchronize()
     o = out.float().cpu().numpy().astype(np.float64)
     l = lse2.cpu().numpy().astype(np.float64)
@@ -81,6 +82,20 @@ def compare(case, out, lse2, ref, lref, what=""):
         if int(case.context_lens[b]) == 0:
             assert np.all(out[b] == 0) and np.all(lse2[b] == -np.inf)
     return summary
+
+
+def sync_records(plan):
+    """The fused hand-off records of a plan: [batch, 8 head groups, 8] uint64."""
+    return plan.sync.cpu().numpy().view(np.uint64).reshape(-1, 8, 8)
+
+
+def check_sync_quiet(plan, what=""):
+    """After a completed fused call: started == its base, arrived == its base,
+    no wait ran out."""
+    rec = sync_records(plan)
+    assert np.all(rec[..., 1] == rec[..., 0]), (what, rec[..., :4])
+    assert np.all(rec[..., 3] == rec[..., 2]), (what, rec[..., :4])
+    assert np.all(rec[..., 4] == 0), (what, "waits ran out", rec[..., 4])
 
 
 def rows_of_plan(case, plan):

@@ -202,6 +202,30 @@ def test_decode_partition_host_checks_launch_nothing():
     assert "heads" in mla.mla_last_error() or mla.mla_last_error() == ""
 
 
+def test_decode_fused_host_checks_launch_nothing():
+    lib = mla.load_library()
+    vp = ctypes.c_void_p
+    good = vp(0x10000)
+
+    def call(**kw):
+        a = dict(qa=good, qp=good, ckv=good, kpe=good, nblk=4, tbl=good, maxb=4, ctx=good,
+                 batch=1, heads=16, scale=0.07, dtype=0, P=good, S=good, ind=good, rows=2,
+                 maxr=2, hpw=0, po=good, pl=good, out=good, lo=None, sync=good, dbg=None,
+                 stream=None)
+        a.update(kw)
+        return lib.mla_decode_fused(a["qa"], a["qp"], a["ckv"], a["kpe"], a["nblk"], a["tbl"],
+                                    a["maxb"], a["ctx"], a["batch"], a["heads"], a["scale"],
+                                    a["dtype"], a["P"], a["S"], a["ind"], a["rows"], a["maxr"],
+                                    a["hpw"], a["po"], a["pl"], a["out"], a["lo"], a["sync"],
+                                    a["dbg"], a["stream"])
+    assert call(sync=None) == -1             # split plan without hand-off state
+    assert call(out=None) == -1              # split plan without out
+    assert call(sync=vp(0x10020)) == -4      # sync must be 64-byte aligned
+    assert call(heads=24) == -6
+    assert call(po=None) == -1
+    assert call(batch=0) == 0
+
+
 def test_decode_reduce_host_checks():
     lib = mla.load_library()
     vp = ctypes.c_void_p
