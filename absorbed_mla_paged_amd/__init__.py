@@ -76,13 +76,13 @@ def load_library(path: str | None = None):
     lib.mla_choose_partitions.restype = ctypes.c_int
     lib.mla_partition_range.argtypes = [i32, i32, i32, i32, i32, i32, pi32, pi32]
     lib.mla_partition_range.restype = ctypes.c_int
-    lib.mla_decode_partition.argtypes = [vp, vp, vp, vp, i32, vp, i32, vp, i32, i32,
+    lib.mla_decode_partition.argtypes = [vp, vp, vp, vp, i32, vp, i32, vp, i32, i32, i32,
                                          ctypes.c_float, i32, vp, vp, vp, i32, i32, i32,
                                          vp, vp, vp, vp, vp, vp]
     lib.mla_decode_partition.restype = ctypes.c_int
     lib.mla_decode_reduce.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
     lib.mla_decode_reduce.restype = ctypes.c_int
-    lib.mla_decode_fused.argtypes = [vp, vp, vp, vp, i32, vp, i32, vp, i32, i32,
+    lib.mla_decode_fused.argtypes = [vp, vp, vp, vp, i32, vp, i32, vp, i32, i32, i32,
                                      ctypes.c_float, i32, vp, vp, vp, i32, i32, i32,
                                      vp, vp, vp, vp, vp, vp, vp]
     lib.mla_decode_fused.restype = ctypes.c_int
@@ -203,6 +203,14 @@ def _dtype_code(t) -> int:
     raise MlaError(-6, f"16-bit tensors must be float16 or bfloat16, got {t.dtype}")
 
 
+def _query_shape(q_absorbed, q_len):
+    """(batch, heads per new token, q_len) of [B, Q, H, 512] or [B, Q*H, 512]."""
+    if q_absorbed.dim() == 4:
+        return int(q_absorbed.shape[0]), int(q_absorbed.shape[2]), int(q_absorbed.shape[1])
+    q = int(q_len or 1)
+    return int(q_absorbed.shape[0]), int(q_absorbed.shape[1]) // q, q
+
+
 def _need_cuda(*ts):
     for t in ts:
         if t is not None and not t.is_cuda:
@@ -212,14 +220,16 @@ def _need_cuda(*ts):
 def mla_decode_partition(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens,
                          scale: float, partitions, splits, row_indptr, total_rows: int,
                          max_rows_per_req: int, heads_per_wg: int, partial_out, partial_lse2,
-                         out, lse2_out=None, debug_ranges=None, stream=None):
-    """Launch the partition kernel (see include/mla_decode.h)."""
+                         out, lse2_out=None, debug_ranges=None, stream=None, q_len=None):
+    """Launch the partition kernel (see include/mla_decode.h). q_absorbed is
+    [B, H, 512], or [B, q_len, H, 512] / [B, q_len*H, 512] for several new
+    tokens per request."""
     lib = load_library()
     _need_cuda(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens)
-    B, H = int(q_absorbed.shape[0]), int(q_absorbed.shape[1])
+    B, H, Q = _query_shape(q_absorbed, q_len)
     _check(lib.mla_decode_partition(
         _ptr(q_absorbed), _ptr(q_pe), _ptr(ckv_cache), _ptr(kpe_cache), int(ckv_cache.shape[0]),
-        _ptr(block_table), int(block_table.shape[1]), _ptr(context_lens), B, H,
+        _ptr(block_table), int(block_table.shape[1]), _ptr(context_lens), B, H, Q,
         float(scale), _dtype_code(q_absorbed), _ptr(partitions), _ptr(splits), _ptr(row_indptr),
         int(total_rows), int(max_rows_per_req), int(heads_per_wg), _ptr(partial_out),
         _ptr(partial_lse2), _ptr(out), _ptr(lse2_out), _ptr(debug_ranges), _stream(stream)))
@@ -228,14 +238,14 @@ def mla_decode_partition(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, co
 def mla_decode_fused(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens,
                      scale: float, partitions, splits, row_indptr, total_rows: int,
                      max_rows_per_req: int, heads_per_wg: int, partial_out, partial_lse2,
-                     out, lse2_out, sync, debug_ranges=None, stream=None):
+                     out, lse2_out, sync, debug_ranges=None, stream=None, q_len=None):
     """Partition and merge in one launch (see include/mla_decode.h)."""
     lib = load_library()
     _need_cuda(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens, out)
-    B, H = int(q_absorbed.shape[0]), int(q_absorbed.shape[1])
+    B, H, Q = _query_shape(q_absorbed, q_len)
     _check(lib.mla_decode_fused(
         _ptr(q_absorbed), _ptr(q_pe), _ptr(ckv_cache), _ptr(kpe_cache), int(ckv_cache.shape[0]),
-        _ptr(block_table), int(block_table.shape[1]), _ptr(context_lens), B, H,
+        _ptr(block_table), int(block_table.shape[1]), _ptr(context_lens), B, H, Q,
         float(scale), _dtype_code(q_absorbed), _ptr(partitions), _ptr(splits), _ptr(row_indptr),
         int(total_rows), int(max_rows_per_req), int(heads_per_wg), _ptr(partial_out),
         _ptr(partial_lse2), _ptr(out), _ptr(lse2_out), _ptr(sync), _ptr(debug_ranges),
@@ -261,6 +271,7 @@ class DecodePlan:
         ctx = [int(c) for c in context_lens]
         self.batch = len(ctx)
         self.heads = num_heads
+        self.q_len = int(q_len)
         self.info = mla_choose_partitions(self.batch, num_heads, q_len, ctx, params)
         i32 = torch.int32
         self.partitions = torch.tensor(self.info["P"], dtype=i32, device=device)
@@ -268,9 +279,10 @@ class DecodePlan:
         self.row_indptr = torch.tensor(self.info["row_indptr"], dtype=i32, device=device)
         rows = max(1, self.info["total_rows"])
         if self.info["needs_reduce"]:
-            self.partial_out = torch.empty((rows, num_heads, KV_LORA_RANK), dtype=torch.float32,
+            qrows = self.q_len * num_heads
+            self.partial_out = torch.empty((rows, qrows, KV_LORA_RANK), dtype=torch.float32,
                                            device=device)
-            self.partial_lse2 = torch.empty((rows, num_heads), dtype=torch.float32, device=device)
+            self.partial_lse2 = torch.empty((rows, qrows), dtype=torch.float32, device=device)
         else:
             self.partial_out = self.partial_lse2 = None
         # Hand-off state of the fused launch: zero-filled once, left ready
@@ -292,14 +304,14 @@ def decode(plan: DecodePlan, q_absorbed, q_pe, ckv_cache, kpe_cache, block_table
                          plan.partitions, plan.splits, plan.row_indptr, plan.total_rows,
                          plan.info["max_rows_per_req"], plan.info["heads_per_wg"],
                          plan.partial_out, plan.partial_lse2, out, lse2_out, plan.sync,
-                         debug_ranges, stream)
+                         debug_ranges, stream, q_len=plan.q_len)
         return
     mla_decode_partition(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens, scale,
                          plan.partitions, plan.splits, plan.row_indptr, plan.total_rows,
                          plan.info["max_rows_per_req"], plan.info["heads_per_wg"],
                          plan.partial_out, plan.partial_lse2, out,
                          lse2_out if not plan.info["needs_reduce"] else None,
-                         debug_ranges, stream)
+                         debug_ranges, stream, q_len=plan.q_len)
     if plan.info["needs_reduce"]:
         mla_decode_reduce(plan.partial_out, plan.partial_lse2, plan.row_indptr, plan.batch,
-                          plan.heads, plan.total_rows, out, lse2_out, stream)
+                          plan.q_len * plan.heads, plan.total_rows, out, lse2_out, stream)

@@ -156,7 +156,12 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
   const int blk_lo = (p < P) ? pb0 + min(s * bps, m) : nblk;
   const int blk_hi = (p < P) ? pb0 + min((s + 1) * bps, m) : nblk;
   const int tok_lo = min(blk_lo * BS, n);
-  const int tok_hi = min(blk_hi * BS, n);
+  const int tok_end = min(blk_hi * BS, n);   // the row's range
+  // With several new tokens per request, head group hg belongs to new token
+  // j = head0 / heads_per_query, which sees all but the last q_len - 1 - j
+  // tokens of the context.
+  const int n_vis = max(0, n - (a.q_len - 1 - head0 / a.heads_per_query));
+  const int tok_hi = max(tok_lo, min(tok_end, n_vis));
   const int nblocks = cdiv(tok_hi - tok_lo, BS);   // non-empty blocks
   const int nst = cdiv(nblocks, 2);                 // stages
 
@@ -240,7 +245,7 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
     }
     if (a.debug_ranges && hg == 0 && tid == 0) {
       a.debug_ranges[2 * row] = tok_lo;
-      a.debug_ranges[2 * row + 1] = tok_hi;
+      a.debug_ranges[2 * row + 1] = tok_end;
     }
     if constexpr (FUSED) tail();
     return;
@@ -506,7 +511,7 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
   finish();
   if (a.debug_ranges && hg == 0 && tid == 0) {
     a.debug_ranges[2 * row] = tok_lo;
-    a.debug_ranges[2 * row + 1] = tok_hi;
+    a.debug_ranges[2 * row + 1] = tok_end;
   }
   if constexpr (FUSED) tail();
 }
@@ -535,7 +540,8 @@ namespace {
 int partition_launch(bool fused, const void* q_absorbed, const void* q_pe, const void* ckv_cache,
                      const void* kpe_cache, int32_t num_blocks, const int32_t* block_table,
                      int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch,
-                     int32_t num_heads, float scale, int32_t dtype, const int32_t* partitions,
+                     int32_t num_heads, int32_t q_len, float scale, int32_t dtype,
+                     const int32_t* partitions,
                      const int32_t* splits, const int32_t* row_indptr, int32_t total_rows,
                      int32_t max_rows_per_req, int32_t heads_per_wg, float* partial_out,
                      float* partial_lse2, void* out, float* lse2_out, uint64_t* sync,
@@ -546,6 +552,8 @@ int partition_launch(bool fused, const void* q_absorbed, const void* q_pe, const
     return fail(MLA_E_UNSUPPORTED, "num_heads %d (need a multiple of 16 in [16, 128])",
                 num_heads);
   if (dtype != MLA_F16 && dtype != MLA_BF16) return fail(MLA_E_UNSUPPORTED, "dtype %d", dtype);
+  if (q_len < 1 || q_len > MLA_MAX_QLEN)
+    return fail(MLA_E_UNSUPPORTED, "q_len %d (need 1 .. %d)", q_len, MLA_MAX_QLEN);
   const int32_t hpw = heads_per_wg ? heads_per_wg : default_heads_per_wg(num_heads);
   if (!valid_heads_per_wg(num_heads, hpw))
     return fail(MLA_E_UNSUPPORTED, "heads_per_wg %d for %d heads (16 or 64 dividing it)",
@@ -583,8 +591,12 @@ int partition_launch(bool fused, const void* q_absorbed, const void* q_pe, const
       (debug_ranges && !aligned(debug_ranges, 8)))
     return fail(MLA_E_ALIGN, "int32/fp32 arrays misaligned");
   const bool merge_here = fused && !direct;
+  const int32_t qrows = q_len * num_heads;   // query rows per request
   if (merge_here && hpw != HG)
     return fail(MLA_E_UNSUPPORTED, "fused merge with %d heads per workgroup", hpw);
+  if (merge_here && qrows / hpw > fused::kGroupsPerRequest)
+    return fail(MLA_E_UNSUPPORTED, "fused merge with %d head groups per request (at most %d)",
+                qrows / hpw, fused::kGroupsPerRequest);
 
   part::PartitionArgs a;
   a.q_absorbed = static_cast<const uint16_t*>(q_absorbed);
@@ -598,9 +610,11 @@ int partition_launch(bool fused, const void* q_absorbed, const void* q_pe, const
   a.debug_ranges = debug_ranges;
   a.sync = merge_here ? sync : nullptr;
   a.num_blocks = num_blocks;
-  a.heads = num_heads;
+  a.heads = qrows;
+  a.q_len = q_len;
+  a.heads_per_query = num_heads;
   a.scale_log2 = scale * 1.4426950408889634f;
-  const int32_t groups = num_heads / hpw;
+  const int32_t groups = qrows / hpw;
   const int32_t rows_per_req = direct ? 1 : max_rows_per_req;
 
   const int64_t slots = (int64_t)batch * rows_per_req;
@@ -634,13 +648,14 @@ int partition_launch(bool fused, const void* q_absorbed, const void* q_pe, const
 extern "C" int mla_decode_partition(
     const void* q_absorbed, const void* q_pe, const void* ckv_cache, const void* kpe_cache,
     int32_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
-    const int32_t* context_lens, int32_t batch, int32_t num_heads, float scale, int32_t dtype,
+    const int32_t* context_lens, int32_t batch, int32_t num_heads, int32_t q_len, float scale,
+    int32_t dtype,
     const int32_t* partitions, const int32_t* splits, const int32_t* row_indptr,
     int32_t total_rows, int32_t max_rows_per_req, int32_t heads_per_wg, float* partial_out,
     float* partial_lse2, void* out, float* lse2_out, int32_t* debug_ranges,
     hipStream_t stream) {
   return partition_launch(false, q_absorbed, q_pe, ckv_cache, kpe_cache, num_blocks, block_table,
-                          max_blocks_per_seq, context_lens, batch, num_heads, scale, dtype,
+                          max_blocks_per_seq, context_lens, batch, num_heads, q_len, scale, dtype,
                           partitions, splits, row_indptr, total_rows, max_rows_per_req,
                           heads_per_wg, partial_out, partial_lse2, out, lse2_out, nullptr,
                           debug_ranges, stream);
@@ -649,13 +664,14 @@ extern "C" int mla_decode_partition(
 extern "C" int mla_decode_fused(
     const void* q_absorbed, const void* q_pe, const void* ckv_cache, const void* kpe_cache,
     int32_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
-    const int32_t* context_lens, int32_t batch, int32_t num_heads, float scale, int32_t dtype,
+    const int32_t* context_lens, int32_t batch, int32_t num_heads, int32_t q_len, float scale,
+    int32_t dtype,
     const int32_t* partitions, const int32_t* splits, const int32_t* row_indptr,
     int32_t total_rows, int32_t max_rows_per_req, int32_t heads_per_wg, float* partial_out,
     float* partial_lse2, void* out, float* lse2_out, uint64_t* sync, int32_t* debug_ranges,
     hipStream_t stream) {
   return partition_launch(true, q_absorbed, q_pe, ckv_cache, kpe_cache, num_blocks, block_table,
-                          max_blocks_per_seq, context_lens, batch, num_heads, scale, dtype,
+                          max_blocks_per_seq, context_lens, batch, num_heads, q_len, scale, dtype,
                           partitions, splits, row_indptr, total_rows, max_rows_per_req,
                           heads_per_wg, partial_out, partial_lse2, out, lse2_out, sync,
                           debug_ranges, stream);

@@ -23,7 +23,9 @@ struct PartitionArgs {
   int32_t* debug_ranges;
   uint64_t* sync;    // merge hand-off state (fused launches only)
   int32_t num_blocks;
-  int32_t heads;
+  int32_t heads;           // query rows per request: q_len * heads_per_query
+  int32_t q_len;           // new tokens per request (1 for plain decode)
+  int32_t heads_per_query; // attention heads of one new token
   float scale_log2;  // scale * log2(e)
 };
 
@@ -48,7 +50,8 @@ struct RowInfo {
   int b;        // request
   int row;      // partial row (request b when the launch is single pass)
   int hg;       // head group
-  int tok_lo, tok_hi;
+  int tok_lo, tok_hi;   // tokens this head group sees in the row
+  int tok_end;          // end of the row's range itself (for debug_ranges)
   int blk_lo;   // first block of the range (request-local)
   int nblocks;  // blocks holding at least one visible token
 };
@@ -70,8 +73,11 @@ __device__ __forceinline__ bool slot_of(int L, int groups, int rows_per_req, int
 }
 
 // Row metadata in one round of scalar loads, then the index math of
-// mla_partition_range (must agree with it bit for bit).
-__device__ __forceinline__ bool find_row(int b, int x, int direct, int total_rows,
+// mla_partition_range (must agree with it bit for bit). The row's range is
+// cut from the whole context; `hidden` more tokens at its end are masked for
+// this head group (new token j of a window of q_len sees all but the last
+// q_len - 1 - j).
+__device__ __forceinline__ bool find_row(int b, int x, int direct, int total_rows, int hidden,
                                          int max_blocks, const int32_t* context_lens,
                                          const int32_t* row_indptr,
                                          const int32_t* partitions, const int32_t* splits,
@@ -103,8 +109,10 @@ __device__ __forceinline__ bool find_row(int b, int x, int direct, int total_row
   const int blk_hi = (p < P) ? pb0 + min((s + 1) * bps, m) : nblk;
   ri->b = b;
   ri->row = row;
+  const int n_vis = max(0, n - hidden);
   ri->tok_lo = min(blk_lo * BS, n);
-  ri->tok_hi = min(blk_hi * BS, n);
+  ri->tok_end = min(blk_hi * BS, n);
+  ri->tok_hi = max(ri->tok_lo, min(ri->tok_end, n_vis));
   ri->blk_lo = blk_lo;
   ri->nblocks = cdiv(ri->tok_hi - ri->tok_lo, BS);
   return true;

@@ -162,8 +162,9 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
   const int hwg = hg * HPW;   // first head of the workgroup
 
   RowInfo ri;
-  if (!find_row(b, x, direct, total_rows, max_blocks, context_lens, row_indptr, partitions,
-                splits, &ri))
+  const int hidden = a.q_len - 1 - hwg / a.heads_per_query;   // new token of this group
+  if (!find_row(b, x, direct, total_rows, hidden, max_blocks, context_lens, row_indptr,
+                partitions, splits, &ri))
     return;
   const int row = ri.row;
   const int nblocks = ri.nblocks;
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
   };
   if (a.debug_ranges && hg == 0 && tid == 0) {
     a.debug_ranges[2 * row] = ri.tok_lo;
-    a.debug_ranges[2 * row + 1] = ri.tok_hi;
+    a.debug_ranges[2 * row + 1] = ri.tok_end;
   }
 
   if (nblocks <= 0) {

@@ -114,6 +114,8 @@ int mla_choose_partitions(int32_t batch, int32_t num_heads, int32_t q_len,
 
   if (batch < 0) return fail(MLA_E_SHAPE, "batch %d < 0", batch);
   if (q_len < 1) return fail(MLA_E_SHAPE, "q_len %d < 1", q_len);
+  if (q_len > MLA_MAX_QLEN)
+    return fail(MLA_E_UNSUPPORTED, "q_len %d (at most %d)", q_len, MLA_MAX_QLEN);
   if (block_size != MLA_BLOCK_SIZE)
     return fail(MLA_E_UNSUPPORTED, "block_size %d (only 32 is supported)", block_size);
   if (num_heads < MLA_MIN_HEADS || num_heads > MLA_MAX_HEADS || num_heads % 16)
@@ -142,23 +144,26 @@ int mla_choose_partitions(int32_t batch, int32_t num_heads, int32_t q_len,
   for (int32_t b = 0; b < batch; ++b)
     if (ctx[b] < 0) return fail(MLA_E_RANGE, "context_lens[%d] = %d < 0", b, ctx[b]);
 
-  const int64_t G = num_heads / hpw;
+  // Workgroups per row: every query row of the request (q_len x heads) is
+  // covered by head groups of hpw rows.
+  const int64_t qrows = int64_t(q_len) * num_heads;
+  const int64_t G = qrows / hpw;
   std::vector<int64_t> nblk(batch), P(batch), S(batch);
   int64_t total_blocks = 0;
   for (int32_t b = 0; b < batch; ++b) {
     nblk[b] = cdiv(ctx[b], MLA_BLOCK_SIZE);
     total_blocks += nblk[b];
   }
-  const bool autoP = q_len == 1 && prm.force_partitions == 0;
-  const bool autoS = q_len == 1 && prm.force_splits == 0;
+  const bool autoP = prm.force_partitions == 0;
+  const bool autoS = prm.force_splits == 0;
   int64_t tile = prm.min_tile_blocks;
   auto splits_for = [&](int64_t nb, int64_t p) {
     return std::max<int64_t>(1, cdiv(cdiv(nb, p), tile));
   };
-  if (q_len != 1) {
-    for (int32_t b = 0; b < batch; ++b) P[b] = S[b] = 1;
-  } else {
-    const bool eligible = int64_t(batch) * G < num_cus;
+  {
+    // The policy split is for pure decode only; several new tokens per
+    // request keep P_b = 1 but are still tiled for the device.
+    const bool eligible = q_len == 1 && int64_t(batch) * G < num_cus;
     for (int32_t b = 0; b < batch; ++b) {
       if (!autoP) P[b] = prm.force_partitions;
       else if (eligible && ctx[b] >= prm.min_split_ctx)
@@ -202,7 +207,7 @@ int mla_choose_partitions(int32_t batch, int32_t num_heads, int32_t q_len,
       rows += P[b] * S[b];
       multi = multi || P[b] * S[b] > 1;
     }
-    return multi ? rows * num_heads * (MLA_KV_LORA_RANK + 1) * 4 : 0;
+    return multi ? rows * qrows * (MLA_KV_LORA_RANK + 1) * 4 : 0;
   };
   const int64_t limit = prm.workspace_limit_bytes;
   if (limit > 0 && workspace() > limit) {
@@ -252,8 +257,8 @@ int mla_choose_partitions(int32_t batch, int32_t num_heads, int32_t q_len,
     info->groups = static_cast<int32_t>(G);
     info->tile_blocks = static_cast<int32_t>(tile);
     info->needs_reduce = ws > 0;
-    info->partial_out_bytes = ws > 0 ? rows * num_heads * MLA_KV_LORA_RANK * 4 : 0;
-    info->partial_lse_bytes = ws > 0 ? rows * num_heads * 4 : 0;
+    info->partial_out_bytes = ws > 0 ? rows * qrows * MLA_KV_LORA_RANK * 4 : 0;
+    info->partial_lse_bytes = ws > 0 ? rows * qrows * 4 : 0;
   }
   return MLA_OK;
 }

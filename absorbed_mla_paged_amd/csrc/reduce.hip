@@ -170,9 +170,10 @@ extern "C" int mla_decode_reduce(const float* partial_out, const float* partial_
                                  hipStream_t stream) {
   clear_error();
   if (batch < 0 || total_rows < 0) return fail(MLA_E_SHAPE, "batch %d, total_rows %d", batch, total_rows);
-  if (num_heads < MLA_MIN_HEADS || num_heads > MLA_MAX_HEADS || num_heads % 16)
-    return fail(MLA_E_UNSUPPORTED, "num_heads %d (need a multiple of 16 in [16, 128])",
-                num_heads);
+  // num_heads counts query rows per request: q_len * heads.
+  if (num_heads < MLA_MIN_HEADS || num_heads > MLA_MAX_HEADS * MLA_MAX_QLEN || num_heads % 16)
+    return fail(MLA_E_UNSUPPORTED, "num_heads %d (need a multiple of 16 in [16, %d])",
+                num_heads, MLA_MAX_HEADS * MLA_MAX_QLEN);
   if (dtype != MLA_F16 && dtype != MLA_BF16) return fail(MLA_E_UNSUPPORTED, "dtype %d", dtype);
   if (batch == 0) return MLA_OK;
   if (!row_indptr || !out || (total_rows > 0 && (!partial_out || !partial_lse2)))

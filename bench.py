@@ -82,7 +82,7 @@ def host_chooser_us(case, prm, calls: int = 2000) -> float:
     info = mla._PlanInfo()
     c_prm = prm._c() if prm is not None else None
     pp = ctypes.byref(c_prm) if c_prm is not None else None
-    args = (B, case.heads, 1, ctx, 32, pp, P, S, ind, ctypes.byref(info))
+    args = (B, case.heads, case.q_len, ctx, 32, pp, P, S, ind, ctypes.byref(info))
     fn = lib.mla_choose_partitions
     if fn(*args) != 0:
         raise RuntimeError(mla.mla_last_error())
@@ -101,8 +101,9 @@ def algorithmic_bytes(case):
     tokens = int(case.context_lens.astype(np.int64).sum())
     nblk = int(sum((int(n) + 31) // 32 for n in case.context_lens))
     kv = tokens * KV_BYTES_PER_TOKEN
-    q = case.batch * case.heads * (512 + 64) * 2
-    out = case.batch * case.heads * 512 * 2
+    rows = case.batch * case.q_len * case.heads   # query rows: new tokens x heads
+    q = rows * (512 + 64) * 2
+    out = rows * 512 * 2
     meta = nblk * 4 + case.batch * 4
     return dict(kv=kv, q=q, out=out, meta=meta, total=kv + q + out + meta,
                 partition=kv + q + meta, tokens=tokens)
@@ -181,10 +182,11 @@ def main():
     table = torch.from_numpy(case.block_table).to(dev)
     ctx = torch.from_numpy(case.context_lens).to(dev)
     prm = mla.PlanParams(force_partitions=1, force_splits=1) if args.single_pass else None
-    plan = mla.DecodePlan(case.context_lens, case.heads, prm, device=dev)
+    plan = mla.DecodePlan(case.context_lens, case.heads, prm, device=dev, q_len=case.q_len)
+    qrows = case.q_len * case.heads
     info = plan.info
-    out = torch.empty((case.batch, case.heads, 512), dtype=td, device=dev)
-    lse2 = torch.empty((case.batch, case.heads), dtype=torch.float32, device=dev)
+    out = torch.empty((case.batch, qrows, 512), dtype=td, device=dev)
+    lse2 = torch.empty((case.batch, qrows), dtype=torch.float32, device=dev)
     log(f"[bench] plan P={info['P']} S={info['S']} rows={info['total_rows']} "
         f"tile={info['tile_blocks']} reduce={info['needs_reduce']} copies={ncopy} "
         f"pool={pool_bytes / 1e6:.1f} MB")
@@ -192,7 +194,7 @@ def main():
     def step(j):
         # Host chooser (same contexts every step, so the device plan arrays
         # already hold its answer), then the device work.
-        mla.mla_choose_partitions(case.batch, case.heads, 1, case.context_lens, prm)
+        mla.mla_choose_partitions(case.batch, case.heads, case.q_len, case.context_lens, prm)
         c, k = copies[j % ncopy]
         mla.decode(plan, qa, qp, c, k, table, ctx, case.scale, out, lse2, fused=args.fused)
 
@@ -249,7 +251,8 @@ def main():
             mla.mla_decode_partition(qa, qp, c, k, table, ctx, case.scale, plan.partitions,
                                      plan.splits, plan.row_indptr, plan.total_rows,
                                      info["max_rows_per_req"], info["heads_per_wg"],
-                                     plan.partial_out, plan.partial_lse2, out, lse2)
+                                     plan.partial_out, plan.partial_lse2, out, lse2,
+                                     q_len=plan.q_len)
     kgraph.replay()
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
@@ -259,7 +262,7 @@ def main():
     torch.cuda.synchronize()
     part_us = e0.elapsed_time(e1) * 1e3 / reps
     achieved = alg["partition"] / (part_us * 1e-6) / 1e9
-    split_bytes = info["total_rows"] * case.heads * 513 * 4 if info["needs_reduce"] else 0
+    split_bytes = info["total_rows"] * qrows * 513 * 4 if info["needs_reduce"] else 0
     pair_gbs = alg["total"] / (ms_per_step * 1e-3) / 1e9
     khash = kernel_hash(info["heads_per_wg"])
     meas = MEASURED.get((args.workload, khash))
@@ -291,6 +294,7 @@ def main():
         "dtype": {"f16": "f16", "bf16": "bf16"}[case.dtype],
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": case.batch, "heads": case.heads,
+                   "q_len": case.q_len,
                    "context_lens": [int(n) for n in case.context_lens],
                    "block_size": 32, "kv_lora_rank": 512, "rope_dim": 64,
                    "plan": {"P": info["P"], "S": info["S"], "rows": info["total_rows"]},

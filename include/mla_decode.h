@@ -52,6 +52,7 @@ extern "C" {
 #define MLA_MAX_SPLITS 4096
 #define MLA_MIN_HEADS 16
 #define MLA_MAX_HEADS 128
+#define MLA_MAX_QLEN 8           /* new tokens per request in one decode call */
 /* Bytes of mla_decode_fused's hand-off state per request (8 head groups of
  * 8 counters). */
 #define MLA_FUSED_SYNC_BYTES_PER_REQUEST 512
@@ -99,11 +100,11 @@ typedef struct {
   int32_t total_rows;        /* sum_b P_b * S_b: rows of the partial workspace */
   int32_t max_rows_per_req;  /* max_b P_b * S_b: grid extent of the partition launch */
   int32_t heads_per_wg;      /* heads one partition workgroup covers */
-  int32_t groups;            /* H / heads_per_wg workgroups per row */
+  int32_t groups;            /* q_len * H / heads_per_wg workgroups per row */
   int32_t tile_blocks;       /* device tile size used for S_b, in blocks */
   int32_t needs_reduce;      /* 1 iff some request has more than one row */
-  int64_t partial_out_bytes; /* total_rows * H * 512 * 4, or 0 when no reduce */
-  int64_t partial_lse_bytes; /* total_rows * H * 4, or 0 when no reduce */
+  int64_t partial_out_bytes; /* total_rows * q_len * H * 512 * 4, or 0 when no reduce */
+  int64_t partial_lse_bytes; /* total_rows * q_len * H * 4, or 0 when no reduce */
 } mla_plan_info;
 
 /* Fill *p with the defaults listed above. */
@@ -117,7 +118,7 @@ void mla_default_plan_params(mla_plan_params* p);
  * device tiling S_b >= 1; rows of request b are row_indptr[b] ..
  * row_indptr[b+1]-1, request-major (the request-major o_indptr of the merge
  * contract, mlxcel pull request 995, "How #898's merge kernel is reused").
- * Rule (G = ceil(H / heads_per_wg)):
+ * Rule (G = q_len * H / heads_per_wg, the head groups over all query rows):
  *   eligible = q_len == 1 && B * G < num_cus
  *   P_b = force_partitions, else clamp(ceil(n_b / tokens_per_partition),
  *         min_partitions, max_partitions) if eligible && n_b >= min_split_ctx,
@@ -128,13 +129,16 @@ void mla_default_plan_params(mla_plan_params* p);
  *   (auto S only) if G * sum P_b S_b > cap, tile becomes the smallest larger
  *   value with G * sum P_b S_b <= cap, or max_b ceil(nblk_b / P_b) if none
  *   fits, so the grid never spills into a second, nearly empty wave.
- * With q_len != 1 every request gets P_b = S_b = 1. If a workspace limit is
+ * With q_len > 1 (several new tokens per request) the policy split stays
+ * P_b = 1, since it is for pure decode only (vllm-metal pull request 601,
+ * "What changed"), and S_b tiles as above. If a workspace limit is
  * set and exceeded: double the tile until it fits or all S_b = 1 (auto S
  * only); then lower the largest P_b by one (lowest b first) down to 2; then
  * set P_b = 1 in ascending n_b order (auto P only). When every request has
  * one row the decode writes `out` directly and needs no workspace.
  *
- * batch >= 0; num_heads in [16, 128], a multiple of 16; q_len >= 1;
+ * batch >= 0; num_heads in [16, 128], a multiple of 16; 1 <= q_len <=
+ * MLA_MAX_QLEN;
  * context_lens_host[b] >= 0; block_size == 32. params may be NULL
  * (defaults). partitions_host, splits_host [batch] and row_indptr_host
  * [batch+1] are written; info may be NULL.
@@ -179,8 +183,18 @@ int mla_partition_range(int32_t ctx, int32_t block_size, int32_t P, int32_t S,
  * may be NULL (vllm-metal pull request 601, "What changed": partition 0
  * writes directly into the final output).
  *
- * q_absorbed  dev [batch, num_heads, 512]     16-bit, 16-byte aligned
- * q_pe        dev [batch, num_heads, 64]      16-bit, 16-byte aligned
+ * Several new tokens per request (q_len > 1, e.g. a speculative window):
+ * the cache already holds all of them, so new token j sits at position
+ * n_b - q_len + j and attends to positions 0 .. n_b - q_len + j (causal
+ * inside the window). Query rows are token-major: row j * num_heads + h is
+ * head h of new token j, in q_absorbed, q_pe, out, lse2_out and the
+ * partials alike. A new token that sees no position gets zeros and -inf.
+ * (The pages decode one token; this generalisation is ours.)
+ *
+ * num_heads   heads per new token: a multiple of 16 in [16, 128]
+ * q_len       new tokens per request, 1 .. MLA_MAX_QLEN (the chooser's q_len)
+ * q_absorbed  dev [batch, q_len, num_heads, 512]  16-bit, 16-byte aligned
+ * q_pe        dev [batch, q_len, num_heads, 64]   16-bit, 16-byte aligned
  * ckv_cache   dev [num_blocks, 32, 512]       16-bit, 16-byte aligned
  * kpe_cache   dev [num_blocks, 32, 64]        16-bit, 16-byte aligned
  * block_table dev int32 [batch, max_blocks_per_seq]; entries below
@@ -195,10 +209,10 @@ int mla_partition_range(int32_t ctx, int32_t block_size, int32_t P, int32_t S,
  *             the chooser's arrays, copied to the device by the caller.
  * total_rows, max_rows_per_req: from mla_plan_info.
  * heads_per_wg: from mla_plan_info (0 = library default for num_heads).
- * partial_out dev fp32 [total_rows, num_heads, 512] (16-byte aligned),
- * partial_lse2 dev fp32 [total_rows, num_heads]
- * out         dev 16-bit [batch, num_heads, 512] (single pass only)
- * lse2_out    dev fp32 [batch, num_heads] or NULL (single pass only)
+ * partial_out dev fp32 [total_rows, q_len * num_heads, 512] (16-byte aligned),
+ * partial_lse2 dev fp32 [total_rows, q_len * num_heads]
+ * out         dev 16-bit [batch, q_len * num_heads, 512] (single pass only)
+ * lse2_out    dev fp32 [batch, q_len * num_heads] or NULL (single pass only)
  * debug_ranges dev int32 [total_rows, 2] or NULL: each row's token range
  *             [begin, end) as the kernel computed it (for bit-exact tests).
  * Errors: MLA_E_NULL, MLA_E_SHAPE, MLA_E_RANGE, MLA_E_ALIGN,
@@ -208,7 +222,7 @@ int mla_decode_partition(const void* q_absorbed, const void* q_pe, const void* c
                          const void* kpe_cache, int32_t num_blocks,
                          const int32_t* block_table, int32_t max_blocks_per_seq,
                          const int32_t* context_lens, int32_t batch, int32_t num_heads,
-                         float scale, int32_t dtype, const int32_t* partitions,
+                         int32_t q_len, float scale, int32_t dtype, const int32_t* partitions,
                          const int32_t* splits, const int32_t* row_indptr,
                          int32_t total_rows, int32_t max_rows_per_req, int32_t heads_per_wg,
                          float* partial_out, float* partial_lse2, void* out, float* lse2_out,
@@ -217,7 +231,7 @@ int mla_decode_partition(const void* q_absorbed, const void* q_pe, const void* c
 /*
  * mla_decode_reduce -- the LSE-weighted reduce kernel (one launch).
  *
- * For each request b and head h over rows r in [row_indptr[b],
+ * For each request b and query row h over rows r in [row_indptr[b],
  * row_indptr[b+1]): M = max lse2_r; if M = -inf the output is 0 and lse2 is
  * -inf; else w_r = 2^(lse2_r - M), out = sum w_r O_r / sum w_r rounded once
  * to nearest-even in `dtype`, lse2_out = M + log2 sum w_r. The summation
@@ -225,6 +239,8 @@ int mla_decode_partition(const void* q_absorbed, const void* q_pe, const void* c
  * request 601, "What changed"; mlxcel pull request 995, "How #898's merge
  * kernel is reused", for base 2 and request-major rows).
  *
+ * num_heads   query rows per request (q_len * heads for several new
+ *             tokens): a multiple of 16 in [16, MLA_MAX_HEADS * MLA_MAX_QLEN]
  * partial_out dev fp32 [total_rows, num_heads, 512], 16-byte aligned
  * partial_lse2 dev fp32 [total_rows, num_heads]
  * row_indptr  dev int32 [batch+1], non-decreasing, row_indptr[0] = 0,
@@ -263,14 +279,16 @@ int mla_decode_reduce(const float* partial_out, const float* partial_lse2,
  *             launch that did not complete it must be zero-filled again.
  *             Word 4 of each 64-byte record counts waits that ran out
  *             (0 in correct use).
- * Currently heads_per_wg must be 16 for split plans (MLA_E_UNSUPPORTED
- * otherwise).
+ * Currently heads_per_wg must be 16 for split plans, with at most 8 head
+ * groups per request (q_len * num_heads <= 128); MLA_E_UNSUPPORTED
+ * otherwise.
  * Errors: as mla_decode_partition.
  */
 int mla_decode_fused(const void* q_absorbed, const void* q_pe, const void* ckv_cache,
                      const void* kpe_cache, int32_t num_blocks, const int32_t* block_table,
                      int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch,
-                     int32_t num_heads, float scale, int32_t dtype, const int32_t* partitions,
+                     int32_t num_heads, int32_t q_len, float scale, int32_t dtype,
+                     const int32_t* partitions,
                      const int32_t* splits, const int32_t* row_indptr, int32_t total_rows,
                      int32_t max_rows_per_req, int32_t heads_per_wg, float* partial_out,
                      float* partial_lse2, void* out, float* lse2_out, uint64_t* sync,

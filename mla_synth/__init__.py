@@ -16,8 +16,10 @@ Recipe (one numpy PCG64 generator per case, draws in this order):
      unless the pool size is given)
   3. ckv pool  [pool, 32, 512]  standard normal float32
   4. kpe pool  [pool, 32, 64]   standard normal float32
-  5. q_absorbed [B, H, 512]     standard normal float32
-  6. q_pe       [B, H, 64]      standard normal float32
+  5. q_absorbed [B, Q*H, 512]   standard normal float32
+  6. q_pe       [B, Q*H, 64]    standard normal float32
+Q (``q_len``, default 1) is the number of new tokens per request: row j*H + h
+is head h of new token j, which sits at position n - Q + j of the context.
 Every float32 draw is multiplied by ``value_scale`` (a power of two, so the
 product is exact) and rounded to nearest-even into the 16-bit storage type.
 Request b's block table is the next ceil(n_b/32) entries of the permutation,
@@ -101,6 +103,7 @@ class Case:
     scale: float
     seed: int
     poisoned: bool = False
+    q_len: int = 1             # new tokens per request; q rows are [B, q_len * H]
 
     @property
     def num_blocks(self) -> int:
@@ -121,7 +124,8 @@ def blocks_for(n: int) -> int:
 def make_case(seed: int, batch: int, heads: int, contexts=None, context_range=None,
               dtype: str = "f16", value_scale: float = 1.0, pool_factor: int = 2,
               pool_blocks: int | None = None, poison: bool = False,
-              scale: float = DEFAULT_SCALE, max_blocks: int | None = None) -> Case:
+              scale: float = DEFAULT_SCALE, max_blocks: int | None = None,
+              q_len: int = 1) -> Case:
     rng = np.random.Generator(np.random.PCG64(seed))
     if context_range is not None:
         lo, hi = context_range
@@ -136,8 +140,8 @@ def make_case(seed: int, batch: int, heads: int, contexts=None, context_range=No
     perm = rng.permutation(pool).astype(np.int32)
     ckv = _draw16(rng, (pool, BLOCK_SIZE, KV_LORA_RANK), dtype, value_scale)
     kpe = _draw16(rng, (pool, BLOCK_SIZE, ROPE_DIM), dtype, value_scale)
-    qa = _draw16(rng, (batch, heads, KV_LORA_RANK), dtype, value_scale)
-    qp = _draw16(rng, (batch, heads, ROPE_DIM), dtype, value_scale)
+    qa = _draw16(rng, (batch, q_len * heads, KV_LORA_RANK), dtype, value_scale)
+    qp = _draw16(rng, (batch, q_len * heads, ROPE_DIM), dtype, value_scale)
 
     width = max(1, max(nblk) if nblk else 1)
     if max_blocks is not None:
@@ -156,7 +160,7 @@ def make_case(seed: int, batch: int, heads: int, contexts=None, context_range=No
 
     case = Case(dtype=dtype, batch=batch, heads=heads, context_lens=ctx,
                 block_table=table, ckv_pool=ckv, kpe_pool=kpe, q_absorbed=qa,
-                q_pe=qp, scale=float(scale), seed=seed)
+                q_pe=qp, scale=float(scale), seed=seed, q_len=int(q_len))
     if poison:
         poison_case(case)
     return case
@@ -200,6 +204,14 @@ WORKLOADS = {
     # Mixed batch: B=8, H=128, contexts uniform in [4096, 131072], bf16.
     "mixed_b8": dict(seed=1005, batch=8, heads=128, context_range=(4096, 131072),
                      dtype="bf16"),
+    # Several new tokens per request (multi-token decode: MTP / speculative
+    # verification windows) at the V2-Lite and V3 shapes.
+    "v2lite_32k_q2": dict(seed=1006, batch=1, heads=16, contexts=[32768], dtype="f16",
+                          q_len=2),
+    "v2lite_32k_q4": dict(seed=1006, batch=1, heads=16, contexts=[32768], dtype="f16",
+                          q_len=4),
+    "v3_131k_q2": dict(seed=1007, batch=1, heads=128, contexts=[131072], dtype="bf16",
+                       value_scale=0.5, q_len=2),
 }
 
 

@@ -58,6 +58,35 @@ def latent_brute(case, b: int, h: int):
     return [x / den for x in num], mpmath.log(den) / mpmath.log(2)
 
 
+def latent_brute_window(case, b: int, j: int, h: int):
+    """Head h of new token j in a window of case.q_len new tokens, by the
+    definition with an explicit causal mask: token j sits at position
+    pos = n - q_len + j and every t > pos is skipped."""
+    n = int(case.context_lens[b])
+    pos = n - int(case.q_len) + j
+    row = j * case.heads + h
+    qa = [_bits_to_mpf(v, case.dtype) for v in case.q_absorbed[b][row]]
+    qp = [_bits_to_mpf(v, case.dtype) for v in case.q_pe[b][row]]
+    scale = mpmath.mpf(case.scale)
+    num = [mpmath.mpf(0)] * len(qa)
+    den = mpmath.mpf(0)
+    for t in range(n):
+        if t > pos:
+            continue
+        phys = int(case.block_table[b][t // 32])
+        c = _row(case.ckv_pool, phys, t % 32, case.dtype)
+        k = _row(case.kpe_pool, phys, t % 32, case.dtype)
+        s = scale * (mpmath.fsum(x * y for x, y in zip(qa, c))
+                     + mpmath.fsum(x * y for x, y in zip(qp, k)))
+        e = mpmath.exp(s)
+        den += e
+        for i in range(len(num)):
+            num[i] += e * c[i]
+    if den == 0:
+        return [mpmath.mpf(0)] * len(qa), mpmath.mpf("-inf")
+    return [x / den for x in num], mpmath.log(den) / mpmath.log(2)
+
+
 def decompressed_brute(case, b: int, h: int, q_nope, W_UK, W_UV_T):
     """Pre-absorption attention for one (b, h) by the definition.
 

@@ -10,7 +10,8 @@ for pure decode, a long enough context, a small decode launch, 2 to 8
 partitions and bounded temporary memory; "Serving sanity check" paragraph
 before the grid: the split path starts at 32K+ context). The rule:
 
-  G          = ceil(H / heads_per_wg)          workgroups per row
+  G          = q_len * H / heads_per_wg       workgroups per row (every
+               query row of the request: q_len new tokens x H heads)
   eligible   = q_len == 1 and B * G < num_cus  pure decode, small launch
   P_b        = force_P, else clamp(ceil(n_b / tokens_per_partition),
                min_P, max_P) if eligible and n_b >= min_split_ctx, else 1
@@ -21,8 +22,10 @@ before the grid: the split path starts at 32K+ context). The rule:
                the smallest larger one with G * sum_b P_b * S_b <= cap, or,
                if none fits, max_b ceil(nblk_b / P_b) (every S_b = 1)
   rows       = sum_b P_b * S_b, request-major (row_indptr)
-  workspace  = rows * H * (512 + 1) * 4 bytes if any P_b * S_b > 1, else 0
-If q_len != 1 every request gets P_b = S_b = 1 (no split at all).
+  workspace  = rows * q_len * H * (512 + 1) * 4 bytes if any P_b * S_b > 1,
+               else 0
+With q_len > 1 the policy keeps P_b = 1 (the split is for pure decode only),
+and the device tiling S_b applies as for one token. q_len is at most 8.
 
 Workspace shedding, when a limit is set and exceeded, in order:
   1. (auto S only) double the tile until the limit holds or every S_b = 1;
@@ -46,6 +49,7 @@ BLOCK_SIZE = 32
 LATENT = 512
 MAX_PARTITIONS = 8
 MAX_SPLITS = 4096
+MAX_QLEN = 8
 
 
 def _cdiv(a: int, b: int) -> int:
@@ -106,7 +110,7 @@ def choose_partitions(batch: int, heads: int, q_len: int, ctx, params: PlanParam
                       block_size: int = BLOCK_SIZE):
     """Mirror of mla_choose_partitions. Raises ValueError on invalid input."""
     prm = params or PlanParams()
-    if batch < 0 or q_len < 1 or block_size != BLOCK_SIZE:
+    if batch < 0 or q_len < 1 or q_len > MAX_QLEN or block_size != BLOCK_SIZE:
         raise ValueError("shape")
     if heads < 16 or heads > 128 or heads % 16:
         raise ValueError("unsupported heads")
@@ -125,17 +129,12 @@ def choose_partitions(batch: int, heads: int, q_len: int, ctx, params: PlanParam
     hpw = prm.heads_per_wg or default_heads_per_wg(heads)
     if hpw not in (16, 64) or heads % hpw:
         raise ValueError("heads per workgroup")
-    G = heads // hpw
+    G = q_len * heads // hpw
     nblk = [_cdiv(n, block_size) for n in ctx]
     total_blocks = sum(nblk)
 
-    if q_len != 1:
-        P = [1] * batch
-        S = [1] * batch
-        tile = max(prm.min_tile_blocks, 1)
-        autoP = autoS = False
-    else:
-        eligible = batch * G < prm.num_cus
+    if True:
+        eligible = q_len == 1 and batch * G < prm.num_cus
         autoP = prm.force_partitions == 0
         autoS = prm.force_splits == 0
         P = []
@@ -173,7 +172,7 @@ def choose_partitions(batch: int, heads: int, q_len: int, ctx, params: PlanParam
     def workspace():
         rows = sum(p * s for p, s in zip(P, S))
         if any(p * s > 1 for p, s in zip(P, S)):
-            return rows * heads * (LATENT + 1) * 4
+            return rows * q_len * heads * (LATENT + 1) * 4
         return 0
 
     limit = prm.workspace_limit_bytes

@@ -74,24 +74,44 @@ def _attend(qa, qp, C, Kp, scale):
     return out, lse2
 
 
+def visible_len(n: int, q_len: int, j: int) -> int:
+    """Tokens new token j of a window of q_len sees in a context of n.
+
+    The cache write comes before attention (vllm-metal pull request 601,
+    "Wrapper benchmark": the timed step writes the new token's KV, then
+    attends), so n counts all q_len new tokens and token j sits at position
+    n - q_len + j. Within the window attention is causal: token j sees
+    positions 0 .. n - q_len + j. Our reading; the pages decode one token.
+    """
+    return max(0, n - q_len + 1 + j)
+
+
 def latent_one(case, b: int, heads=None, lo: int = 0, hi: int | None = None):
-    """Oracle output for request b (optionally a head subset / token range)."""
+    """Oracle output for request b (optionally a subset of query rows / a
+    token range). Query row j * H + h is head h of new token j."""
     n = int(case.context_lens[b])
-    heads = np.arange(case.heads) if heads is None else np.asarray(heads)
-    C, Kp = gather_request(case.ckv_pool, case.kpe_pool, case.block_table[b], n,
-                           case.dtype, lo, hi)
-    qa = decode16(case.q_absorbed[b, heads], case.dtype)
-    qp = decode16(case.q_pe[b, heads], case.dtype)
-    return _attend(qa, qp, C, Kp, case.scale)
+    q_len = int(getattr(case, "q_len", 1))
+    rows = np.arange(q_len * case.heads) if heads is None else np.asarray(heads)
+    hi = n if hi is None else hi
+    out = np.zeros((rows.size, LATENT))
+    lse2 = np.zeros(rows.size)
+    for j in sorted(set((rows // case.heads).tolist())):
+        sel = rows // case.heads == j
+        C, Kp = gather_request(case.ckv_pool, case.kpe_pool, case.block_table[b], n,
+                               case.dtype, lo, min(hi, visible_len(n, q_len, j)))
+        qa = decode16(case.q_absorbed[b, rows[sel]], case.dtype)
+        qp = decode16(case.q_pe[b, rows[sel]], case.dtype)
+        out[sel], lse2[sel] = _attend(qa, qp, C, Kp, case.scale)
+    return out, lse2
 
 
 def latent_f64(case, requests=None, heads=None):
     """Single-pass absorbed decode for a whole batch (or a sample of it).
 
-    Returns out [B, H, 512] and lse2 [B, H]; entries outside the requested
-    sample are NaN.
+    Returns out [B, q_len * H, 512] and lse2 [B, q_len * H]; entries outside
+    the requested sample are NaN.
     """
-    B, H = case.batch, case.heads
+    B, H = case.batch, int(getattr(case, "q_len", 1)) * case.heads
     out = np.full((B, H, LATENT), np.nan)
     lse2 = np.full((B, H), np.nan)
     reqs = range(B) if requests is None else requests
@@ -118,6 +138,7 @@ def decompressed_f64(case, q_nope, W_UK, W_UV_T, requests=None):
     score = scale * [q_nope ; q_pe] . key_t, output = softmax-weighted
     values. Returns o [B, H, dv], lse2 [B, H].
     """
+    assert int(getattr(case, "q_len", 1)) == 1, "pre-absorption path: one new token"
     B, H = case.batch, case.heads
     dv = W_UV_T.shape[2]
     o = np.full((B, H, dv), np.nan)
@@ -186,7 +207,7 @@ def partials_f64(case, ranges, row_indptr):
     Returns partial_out [rows, H, 512], partial_lse2 [rows, H].
     """
     rows = len(ranges)
-    H = case.heads
+    H = int(getattr(case, "q_len", 1)) * case.heads
     po = np.zeros((rows, H, LATENT))
     pl = np.full((rows, H), -np.inf)
     for r, (b, lo, hi) in enumerate(ranges):

@@ -46,9 +46,11 @@ def run_case(case, params: mla.PlanParams | None = None, dev=None, want_ranges=F
     """Plan on the host, decode on the GPU; returns (out f64, lse2 f64, plan, ranges)."""
     import torch
     dev = dev or to_device(case)
-    plan = mla.DecodePlan(case.context_lens, case.heads, params)
-    out = torch.empty((case.batch, case.heads, 512), dtype=torch_dtype(case.dtype), device="cuda")
-    lse2 = torch.empty((case.batch, case.heads), dtype=torch.float32, device="cuda")
+    q_len = int(getattr(case, "q_len", 1))
+    plan = mla.DecodePlan(case.context_lens, case.heads, params, q_len=q_len)
+    rows = q_len * case.heads
+    out = torch.empty((case.batch, rows, 512), dtype=torch_dtype(case.dtype), device="cuda")
+    lse2 = torch.empty((case.batch, rows), dtype=torch.float32, device="cuda")
     ranges = None
     if want_ranges:
         ranges = torch.full((max(1, plan.total_rows), 2), -7, dtype=torch.int32, device="cuda")

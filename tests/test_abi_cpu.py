@@ -121,6 +121,11 @@ def test_chooser_pure_decode_and_errors():
     assert ref is None and got is None
     ref, got = _both(1, 16, 0, [10], num_cus=256)
     assert ref is None and got is None
+    ref, got = _both(1, 16, 9, [10], num_cus=256)
+    assert ref is None and got is None
+    for q in (2, 4, 8):
+        _same(*_both(3, 32, q, [40000, 7, 3000], num_cus=256))
+        _same(*_both(1, 128, q, [131072], num_cus=256))
     with pytest.raises(mla.MlaError) as e:
         mla.mla_choose_partitions(1, 16, 1, [10], mla.PlanParams(num_cus=256), block_size=16)
     assert e.value.status == -6
@@ -174,16 +179,19 @@ def test_decode_partition_host_checks_launch_nothing():
 
     def call(**kw):
         a = dict(qa=good, qp=good, ckv=good, kpe=good, nblk=4, tbl=good, maxb=4, ctx=good,
-                 batch=1, heads=16, scale=0.07, dtype=0, P=good, S=good, ind=good, rows=2,
+                 batch=1, heads=16, qlen=1, scale=0.07, dtype=0, P=good, S=good, ind=good, rows=2,
                  maxr=2, hpw=0, po=good, pl=good, out=good, lo=None, dbg=None, stream=None)
         a.update(kw)
         return lib.mla_decode_partition(a["qa"], a["qp"], a["ckv"], a["kpe"], a["nblk"], a["tbl"],
-                                        a["maxb"], a["ctx"], a["batch"], a["heads"], a["scale"],
+                                        a["maxb"], a["ctx"], a["batch"], a["heads"], a["qlen"],
+                                        a["scale"],
                                         a["dtype"], a["P"], a["S"], a["ind"], a["rows"], a["maxr"],
                                         a["hpw"], a["po"], a["pl"], a["out"], a["lo"], a["dbg"],
                                         a["stream"])
     assert call(heads=24) == -6
     assert call(heads=160) == -6
+    assert call(qlen=0) == -6
+    assert call(qlen=9) == -6
     assert call(dtype=7) == -6
     assert call(hpw=32) == -6
     assert call(heads=128, hpw=128) == -6   # no 128-head layout
@@ -209,18 +217,20 @@ def test_decode_fused_host_checks_launch_nothing():
 
     def call(**kw):
         a = dict(qa=good, qp=good, ckv=good, kpe=good, nblk=4, tbl=good, maxb=4, ctx=good,
-                 batch=1, heads=16, scale=0.07, dtype=0, P=good, S=good, ind=good, rows=2,
+                 batch=1, heads=16, qlen=1, scale=0.07, dtype=0, P=good, S=good, ind=good, rows=2,
                  maxr=2, hpw=0, po=good, pl=good, out=good, lo=None, sync=good, dbg=None,
                  stream=None)
         a.update(kw)
         return lib.mla_decode_fused(a["qa"], a["qp"], a["ckv"], a["kpe"], a["nblk"], a["tbl"],
-                                    a["maxb"], a["ctx"], a["batch"], a["heads"], a["scale"],
+                                    a["maxb"], a["ctx"], a["batch"], a["heads"], a["qlen"],
+                                    a["scale"],
                                     a["dtype"], a["P"], a["S"], a["ind"], a["rows"], a["maxr"],
                                     a["hpw"], a["po"], a["pl"], a["out"], a["lo"], a["sync"],
                                     a["dbg"], a["stream"])
     assert call(sync=None) == -1             # split plan without hand-off state
     assert call(out=None) == -1              # split plan without out
     assert call(sync=vp(0x10020)) == -4      # sync must be 64-byte aligned
+    assert call(heads=128, hpw=16, qlen=2) == -6   # 16 head groups: more than the record holds
     assert call(heads=24) == -6
     assert call(po=None) == -1
     assert call(batch=0) == 0

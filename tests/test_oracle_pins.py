@@ -10,6 +10,7 @@ import json
 import math
 import os
 
+import mpmath
 import numpy as np
 import pytest
 
@@ -369,3 +370,80 @@ def test_planted_mistakes_are_caught(monkeypatch, mutant):
               "sign": _mutant_attend_sign}[mutant]
         monkeypatch.setattr(reference, "_attend", fn)
     assert not _pins_pass(case)
+
+
+# --- several new tokens per request (the in-window causal mask) ---------------
+# Our reading (no page decodes more than one token): the cache holds all
+# q_len new tokens, token j sits at position n - q_len + j and sees positions
+# 0 .. n - q_len + j.
+
+@pytest.mark.parametrize("dtype,q_len,contexts", [("f16", 3, [40]), ("bf16", 2, [33, 5]),
+                                                  ("f16", 4, [3])])
+def test_window_matches_brute_force(dtype, q_len, contexts):
+    # Each new token by the definition with an explicit causal mask, at 50
+    # digits; [3] with four new tokens leaves the first one nothing to see.
+    case = small_case(141 + q_len, contexts, heads=2, dtype=dtype, q_len=q_len)
+    out, lse2 = oracle.latent_f64(case)
+    assert out.shape == (len(contexts), 2 * q_len, 512)
+    for b in range(len(contexts)):
+        for j in range(q_len):
+            for h in range(2):
+                bo, bl = brute.latent_brute_window(case, b, j, h)
+                r = j * 2 + h
+                if bl == mpmath.mpf("-inf"):
+                    assert lse2[b, r] == -np.inf and np.all(out[b, r] == 0)
+                    continue
+                eo = max(abs(float(x) - o) for x, o in zip(bo, out[b, r]))
+                assert eo < 1e-12 and abs(float(bl) - lse2[b, r]) < 1e-12, (b, j, h)
+
+
+def _window_counts_hold(case, n):
+    out, lse2 = oracle.latent_f64(case)
+    rows = np.stack([reference.decode16(case.ckv_pool[case.block_table[0, t // 32], t % 32],
+                                        case.dtype) for t in range(n)])
+    H = case.heads
+    ok = True
+    for j in range(case.q_len):
+        cnt = n - case.q_len + j + 1          # positions 0 .. n - q_len + j
+        mean = rows[:cnt].sum(axis=0) / cnt
+        ok &= bool(np.max(np.abs(out[0, j * H:(j + 1) * H] - mean[None])) < 1e-13)
+        ok &= bool(np.all(np.abs(lse2[0, j * H:(j + 1) * H] - math.log2(cnt)) < 1e-13))
+    return ok
+
+
+@pytest.mark.parametrize("q_len", [2, 5])
+def test_window_uniform_scores_count(q_len):
+    # q = 0: new token j's output is the plain mean of the rows it sees and
+    # its lse2 is log2 of their number.
+    n = 70
+    case = small_case(151, [n], heads=2, dtype="bf16", poison=True, q_len=q_len)
+    case.q_absorbed[:] = 0
+    case.q_pe[:] = 0
+    assert _window_counts_hold(case, n)
+
+
+def test_window_off_by_one_is_caught(monkeypatch):
+    n = 70
+    case = small_case(152, [n], heads=2, dtype="bf16", q_len=3)
+    case.q_absorbed[:] = 0
+    case.q_pe[:] = 0
+    assert _window_counts_hold(case, n)
+    monkeypatch.setattr(reference, "visible_len", lambda n, q, j: max(0, n - q + j))
+    assert not _window_counts_hold(case, n)
+
+
+def test_window_needle_visibility():
+    # A dominant token at position n - q_len + j is found by new token j and
+    # left unseen by new token j - 1.
+    n, q_len, H = 90, 3, 2
+    for j in range(1, q_len):
+        t = n - q_len + j
+        for row, seen in ((j * H + 1, True), ((j - 1) * H + 1, False)):
+            case = small_case(161, [n], heads=H, q_len=q_len)
+            before, _ = oracle.latent_f64(case)
+            needle = plant_needle(case, 0, t, row)
+            after, _ = oracle.latent_f64(case)
+            if seen:
+                assert np.max(np.abs(after[0, row] - needle)) < 1e-12
+            else:
+                assert np.array_equal(before[0, row], after[0, row])

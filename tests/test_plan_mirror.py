@@ -51,9 +51,16 @@ def test_policy_partition_counts(n, expect):
 
 
 def test_pure_decode_gate():
+    # Two new tokens: no policy split (pure decode only), but the device
+    # tiling still spreads the 2 x 16 query rows' head groups over the CUs.
     r = plan.choose_partitions(1, 16, 2, [131072], plan.PlanParams())
-    assert r["P"] == [1] and r["S"] == [1] and r["needs_reduce"] == 0
-    assert r["workspace_bytes"] == 0
+    assert r["P"] == [1] and r["groups"] == 2
+    assert r["S"] == [128] and r["tile_blocks"] == 32     # 2 * 4096 blocks / 256 CUs
+    assert r["workspace_bytes"] == 128 * 2 * 16 * 513 * 4
+    r1 = plan.choose_partitions(1, 16, 1, [131072], plan.PlanParams())
+    assert r1["P"] == [8]
+    with pytest.raises(ValueError):
+        plan.choose_partitions(1, 16, 9, [1000], plan.PlanParams())
 
 
 def test_small_launch_gate():
