@@ -25,7 +25,8 @@ STATUS = {0: "MLA_OK", -1: "MLA_E_NULL", -2: "MLA_E_SHAPE", -3: "MLA_E_RANGE",
 
 # Every function include/mla_decode.h declares.
 EXPORTS = ["mla_default_plan_params", "mla_choose_partitions", "mla_partition_range",
-           "mla_decode_partition", "mla_decode_reduce", "mla_decode_fused", "mla_status_string",
+           "mla_decode_partition", "mla_decode_reduce", "mla_decode_fused", "mla_absorb_query",
+           "mla_unabsorb_output", "mla_status_string",
            "mla_last_error", "mla_get_counters", "mla_reset_counters"]
 
 
@@ -86,6 +87,9 @@ def load_library(path: str | None = None):
                                      ctypes.c_float, i32, vp, vp, vp, i32, i32, i32,
                                      vp, vp, vp, vp, vp, vp, vp]
     lib.mla_decode_fused.restype = ctypes.c_int
+    for name in ("mla_absorb_query", "mla_unabsorb_output"):
+        getattr(lib, name).argtypes = [vp, vp, vp, i32, i32, i32, vp]
+        getattr(lib, name).restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_last_error.argtypes = []
@@ -260,6 +264,25 @@ def mla_decode_reduce(partial_out, partial_lse2, row_indptr, batch: int, num_hea
     _check(lib.mla_decode_reduce(_ptr(partial_out), _ptr(partial_lse2), _ptr(row_indptr),
                                  int(batch), int(num_heads), int(total_rows), _dtype_code(out),
                                  _ptr(out), _ptr(lse2_out), _stream(stream)))
+
+
+def _head_product(name, x, w, y, stream):
+    lib = load_library()
+    _need_cuda(x, w, y)
+    heads = int(w.shape[0])
+    rows = x.numel() // (heads * int(w.shape[1])) if x.numel() else 0
+    _check(getattr(lib, name)(_ptr(x), _ptr(w), _ptr(y), rows, heads, _dtype_code(x),
+                              _stream(stream)))
+
+
+def mla_absorb_query(q_nope, w_uk, q_absorbed, stream=None):
+    """q_absorbed[..., h, :] = q_nope[..., h, :] @ w_uk[h] (see include/mla_decode.h)."""
+    _head_product("mla_absorb_query", q_nope, w_uk, q_absorbed, stream)
+
+
+def mla_unabsorb_output(out_latent, w_uv_t, o, stream=None):
+    """o[..., h, :] = out_latent[..., h, :] @ w_uv_t[h] (see include/mla_decode.h)."""
+    _head_product("mla_unabsorb_output", out_latent, w_uv_t, o, stream)
 
 
 class DecodePlan:

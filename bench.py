@@ -127,6 +127,63 @@ def cpu_baseline(case, budget_s: float):
                        f"repetitions after one warm-up, {per * reps:.1f} s of wall time")
 
 
+def projections(case, args, torch, mla):
+    """Fold and unfold for the workload's rows (batch x new tokens) and heads,
+    each launch reading its 128 x 512 weights per head from HBM. K launches
+    of each in a graph (weights rotated over copies so the cache cannot hold
+    them), HIP events on the launch stream."""
+    td = torch.float16 if case.dtype == "f16" else torch.bfloat16
+    dev = torch.device("cuda", 0)
+    rows, H = case.batch * case.q_len, case.heads
+    g = torch.Generator(device=dev).manual_seed(1234)
+    wbytes = H * 128 * 512 * 2
+    ncopy = max(1, min(64, math.ceil(args.cold_bytes / (2 * wbytes))))
+    w_uk = [(torch.randn((H, 128, 512), device=dev, generator=g) / 11.3).to(td) for _ in range(ncopy)]
+    w_uv = [(torch.randn((H, 512, 128), device=dev, generator=g) / 22.6).to(td) for _ in range(ncopy)]
+    qn = torch.randn((rows, H, 128), device=dev, generator=g).to(td)
+    lat = torch.randn((rows, H, 512), device=dev, generator=g).to(td)
+    qa = torch.empty((rows, H, 512), dtype=td, device=dev)
+    o = torch.empty((rows, H, 128), dtype=td, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+    res = {}
+    for name, fn, x, ws, y in (("fold", mla.mla_absorb_query, qn, w_uk, qa),
+                               ("unfold", mla.mla_unabsorb_output, lat, w_uv, o)):
+        with torch.cuda.stream(stream):
+            for j in range(args.warmup):
+                fn(x, ws[j % ncopy], y, stream)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=stream):
+            for j in range(args.steps):
+                fn(x, ws[j % ncopy], y, stream)
+        gr.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            gr.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        nbytes = wbytes + x.numel() * 2 + y.numel() * 2
+        res[name] = dict(us=round(us, 3), bytes=nbytes, gbs=round(nbytes / (us * 1e-6) / 1e9, 1))
+        log(f"[bench] {name}: {us:.2f} us, {nbytes / 1e6:.2f} MB -> {res[name]['gbs']:.0f} GB/s")
+    total = res["fold"]["us"] + res["unfold"]["us"]
+    big = max(res.values(), key=lambda r: r["us"])
+    line = {
+        "metric": "per-head fold and unfold latency (us), absorbed-MLA decode",
+        "value": round(total, 3), "unit": "us", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(total * 1e-3, 6), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": case.dtype, "data": "synthetic",
+        "config": {"workload": args.workload, "rows": rows, "heads": H, "weight_copies": ncopy},
+        "kernels": res,
+        "roofline": {"bound": "hbm", "achieved": big["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(big["gbs"] / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,6 +193,9 @@ def main():
     ap.add_argument("--single-pass", action="store_true", help="force P = S = 1")
     ap.add_argument("--fused", action="store_true",
                     help="partition and merge in one launch (mla_decode_fused)")
+    ap.add_argument("--projections", action="store_true",
+                    help="instead: time the per-head fold (q_nope W_UK) and unfold "
+                         "(out W_UV^T) for the workload's batch and heads")
     ap.add_argument("--cold-bytes", type=float, default=1.5e9,
                     help="bytes of distinct KV copies cycled through (MALL is 256 MB)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -166,6 +226,9 @@ def main():
 
     log(f"[bench] workload={args.workload} steps={args.steps} warmup={args.warmup}")
     case = mla_synth.make_workload(args.workload)
+    if args.projections:
+        projections(case, args, torch, mla)
+        return
     alg = algorithmic_bytes(case)
     td = torch.float16 if case.dtype == "f16" else torch.bfloat16
     dev = torch.device("cuda", 0)

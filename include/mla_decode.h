@@ -294,6 +294,32 @@ int mla_decode_fused(const void* q_absorbed, const void* q_pe, const void* ckv_c
                      float* partial_lse2, void* out, float* lse2_out, uint64_t* sync,
                      int32_t* debug_ranges, hipStream_t stream);
 
+/*
+ * mla_absorb_query / mla_unabsorb_output -- the per-head products on either
+ * side of absorbed decode (mlxcel pull request 995, "What changed", the
+ * absorb.rs bullet: kv_b_proj splits into W_UK [H, qk_nope, r], folded into
+ * the query, and W_UV^T [H, r, v_head], applied to the latent output; with
+ * qk_nope = v_head = 128 and r = 512):
+ *   q_absorbed[i, h, :] = q_nope[i, h, :] . W_UK[h]      (128 -> 512)
+ *   o[i, h, :]          = out_latent[i, h, :] . W_UV^T[h] (512 -> 128)
+ * fp32 accumulation in a fixed order, one round-to-nearest-even into the
+ * 16-bit type of the tensors (bit-identical run to run).
+ *
+ * rows        rows of each head: the batch, or batch * q_len for several
+ *             new tokens (token-major rows flatten into the batch), >= 0
+ * num_heads   1 .. MLA_MAX_HEADS * MLA_MAX_QLEN
+ * q_nope      dev 16-bit [rows, num_heads, 128];  w_uk dev [num_heads, 128, 512]
+ * q_absorbed  dev 16-bit [rows, num_heads, 512] (written)
+ * out_latent  dev 16-bit [rows, num_heads, 512];  w_uv_t dev [num_heads, 512, 128]
+ * o           dev 16-bit [rows, num_heads, 128] (written)
+ * All 16-byte aligned; dtype MLA_F16 or MLA_BF16 for every tensor.
+ * Errors: MLA_E_NULL, MLA_E_SHAPE, MLA_E_ALIGN, MLA_E_UNSUPPORTED, MLA_E_HIP.
+ */
+int mla_absorb_query(const void* q_nope, const void* w_uk, void* q_absorbed, int32_t rows,
+                     int32_t num_heads, int32_t dtype, hipStream_t stream);
+int mla_unabsorb_output(const void* out_latent, const void* w_uv_t, void* o, int32_t rows,
+                        int32_t num_heads, int32_t dtype, hipStream_t stream);
+
 /* Text for a status code (static storage). */
 const char* mla_status_string(int status);
 

@@ -236,6 +236,19 @@ def test_decode_fused_host_checks_launch_nothing():
     assert call(batch=0) == 0
 
 
+def test_head_products_host_checks():
+    lib = mla.load_library()
+    vp = ctypes.c_void_p
+    g = vp(0x10000)
+    for fn in (lib.mla_absorb_query, lib.mla_unabsorb_output):
+        assert fn(None, g, g, 2, 16, 0, None) == -1
+        assert fn(g, g, vp(0x10008), 2, 16, 0, None) == -4
+        assert fn(g, g, g, 2, 0, 0, None) == -2
+        assert fn(g, g, g, -1, 16, 0, None) == -2
+        assert fn(g, g, g, 2, 16, 5, None) == -6
+        assert fn(None, None, None, 0, 16, 0, None) == 0   # nothing to do
+
+
 def test_decode_reduce_host_checks():
     lib = mla.load_library()
     vp = ctypes.c_void_p
