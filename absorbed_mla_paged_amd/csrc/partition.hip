@@ -78,7 +78,7 @@ static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 // no argument fetch; the PartitionArgs block is fetched meanwhile.
 template <int DT, bool FUSED>
 __global__ __launch_bounds__(THREADS) void partition_kernel(
-    int32_t groups, int32_t rows_per_req, int32_t slots, int32_t direct, int32_t total_rows,
+    int32_t groups, int32_t rows_per_req, int32_t slots, int32_t flags, int32_t total_rows,
     int32_t max_blocks, const int32_t* __restrict__ context_lens,
     const int32_t* __restrict__ row_indptr, const int32_t* __restrict__ partitions,
     const int32_t* __restrict__ splits, const int32_t* __restrict__ block_table,
@@ -96,6 +96,7 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
   const int ln = lane & 15;   // MFMA row/column inside a 16-wide tile
   const int lg = lane >> 4;   // MFMA k-group (0..3)
   const bool copier = wave >= CWAVES;
+  const int direct = flags & 1;
 
   // ---- which (request, local row, head group) this workgroup owns -------
   // Workgroups are dealt to the 8 XCDs round-robin by linear id. Row slot
@@ -157,10 +158,9 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
   const int blk_hi = (p < P) ? pb0 + min((s + 1) * bps, m) : nblk;
   const int tok_lo = min(blk_lo * BS, n);
   const int tok_end = min(blk_hi * BS, n);   // the row's range
-  // With several new tokens per request, head group hg belongs to new token
-  // j = head0 / heads_per_query, which sees all but the last q_len - 1 - j
-  // tokens of the context.
-  const int n_vis = max(0, n - (a.q_len - 1 - head0 / a.heads_per_query));
+  // With several new tokens per request, this head group belongs to one new
+  // token, which does not see the last hidden_tail() tokens of the context.
+  const int n_vis = max(0, n - hidden_tail(flags, head0));
   const int tok_hi = max(tok_lo, min(tok_end, n_vis));
   const int nblocks = cdiv(tok_hi - tok_lo, BS);   // non-empty blocks
   const int nst = cdiv(nblocks, 2);                 // stages
@@ -611,8 +611,6 @@ int partition_launch(bool fused, const void* q_absorbed, const void* q_pe, const
   a.sync = merge_here ? sync : nullptr;
   a.num_blocks = num_blocks;
   a.heads = qrows;
-  a.q_len = q_len;
-  a.heads_per_query = num_heads;
   a.scale_log2 = scale * 1.4426950408889634f;
   const int32_t groups = qrows / hpw;
   const int32_t rows_per_req = direct ? 1 : max_rows_per_req;
@@ -622,7 +620,7 @@ int partition_launch(bool fused, const void* q_absorbed, const void* q_pe, const
   if (wgs > INT32_MAX || slots > INT32_MAX)
     return fail(MLA_E_SHAPE, "grid too large (%lld workgroups)", (long long)wgs);
   const dim3 grid((unsigned)wgs), block(THREADS);
-  const int32_t dflag = direct ? 1 : 0, sl = (int32_t)slots;
+  const int32_t dflag = part::pack_flags(direct, q_len, num_heads), sl = (int32_t)slots;
   if (hpw != HG)
     part::launch_wide(dtype, hpw, (unsigned)wgs, stream, groups, rows_per_req, sl, dflag,
                       total_rows, max_blocks_per_seq, context_lens, row_indptr, partitions,

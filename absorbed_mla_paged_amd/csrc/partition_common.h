@@ -23,11 +23,26 @@ struct PartitionArgs {
   int32_t* debug_ranges;
   uint64_t* sync;    // merge hand-off state (fused launches only)
   int32_t num_blocks;
-  int32_t heads;           // query rows per request: q_len * heads_per_query
-  int32_t q_len;           // new tokens per request (1 for plain decode)
-  int32_t heads_per_query; // attention heads of one new token
+  int32_t heads;     // query rows per request: q_len x heads of one new token
   float scale_log2;  // scale * log2(e)
 };
+
+// The `flags` kernel argument (preloaded with the row lookup's arguments):
+// bit 0 single pass (write `out` directly), bits 1..3 q_len - 1, bits 8..
+// heads of one new token.
+constexpr int32_t pack_flags(bool direct, int32_t q_len, int32_t heads_per_query) {
+  return (direct ? 1 : 0) | ((q_len - 1) << 1) | (heads_per_query << 8);
+}
+
+#ifdef __HIPCC__
+// Tokens at the end of the context hidden from the head group starting at
+// query row `head0`: new token j = head0 / heads_per_query of a window of
+// q_len sees all but the last q_len - 1 - j.
+__device__ __forceinline__ int hidden_tail(int32_t flags, int head0) {
+  const int qm1 = (flags >> 1) & 7;
+  return qm1 ? qm1 - head0 / (flags >> 8) : 0;
+}
+#endif
 
 constexpr int BS = MLA_BLOCK_SIZE;      // tokens per cache block
 constexpr int LAT = MLA_KV_LORA_RANK;   // 512
@@ -135,7 +150,7 @@ __device__ __forceinline__ void bump_counter(MLA_LDS uint32_t* c, int lane) {
 // Launch of the wide kernel (heads_per_wg 64); arguments as the 16-head
 // kernel's. Host side, after the launcher's checks.
 void launch_wide(int dtype, int hpw, unsigned wgs, hipStream_t stream, int32_t groups,
-                 int32_t rows_per_req, int32_t slots, int32_t direct, int32_t total_rows,
+                 int32_t rows_per_req, int32_t slots, int32_t flags, int32_t total_rows,
                  int32_t max_blocks, const int32_t* context_lens, const int32_t* row_indptr,
                  const int32_t* partitions, const int32_t* splits, const int32_t* block_table,
                  const PartitionArgs& a);

@@ -133,7 +133,7 @@ __device__ __forceinline__ void meet() {
 
 template <int DT>
 __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
-    int32_t groups, int32_t rows_per_req, int32_t slots, int32_t direct, int32_t total_rows,
+    int32_t groups, int32_t rows_per_req, int32_t slots, int32_t flags, int32_t total_rows,
     int32_t max_blocks, const int32_t* __restrict__ context_lens,
     const int32_t* __restrict__ row_indptr, const int32_t* __restrict__ partitions,
     const int32_t* __restrict__ splits, const int32_t* __restrict__ block_table,
@@ -161,10 +161,10 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
   if (!slot_of(blockIdx.x, groups, rows_per_req, slots, &b, &x, &hg)) return;
   const int hwg = hg * HPW;   // first head of the workgroup
 
+  const int direct = flags & 1;
   RowInfo ri;
-  const int hidden = a.q_len - 1 - hwg / a.heads_per_query;   // new token of this group
-  if (!find_row(b, x, direct, total_rows, hidden, max_blocks, context_lens, row_indptr,
-                partitions, splits, &ri))
+  if (!find_row(b, x, direct, total_rows, hidden_tail(flags, hwg), max_blocks, context_lens,
+                row_indptr, partitions, splits, &ri))
     return;
   const int row = ri.row;
   const int nblocks = ri.nblocks;
@@ -597,18 +597,18 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
 }  // namespace
 
 void launch_wide(int dtype, int hpw, unsigned wgs, hipStream_t stream, int32_t groups,
-                 int32_t rows_per_req, int32_t slots, int32_t direct, int32_t total_rows,
+                 int32_t rows_per_req, int32_t slots, int32_t flags, int32_t total_rows,
                  int32_t max_blocks, const int32_t* context_lens, const int32_t* row_indptr,
                  const int32_t* partitions, const int32_t* splits, const int32_t* block_table,
                  const PartitionArgs& a) {
   (void)hpw;  // 64: the only wide layout
   if (dtype == MLA_F16)
     hipLaunchKernelGGL(wide_kernel<0>, dim3(wgs), dim3(THREADS), 0, stream, groups, rows_per_req,
-                       slots, direct, total_rows, max_blocks, context_lens, row_indptr,
+                       slots, flags, total_rows, max_blocks, context_lens, row_indptr,
                        partitions, splits, block_table, a);
   else
     hipLaunchKernelGGL(wide_kernel<1>, dim3(wgs), dim3(THREADS), 0, stream, groups, rows_per_req,
-                       slots, direct, total_rows, max_blocks, context_lens, row_indptr,
+                       slots, flags, total_rows, max_blocks, context_lens, row_indptr,
                        partitions, splits, block_table, a);
 }
 
