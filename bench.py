@@ -46,9 +46,9 @@ FETCH_SCALE = 2.0
 WRITE_SCALE = 1.0
 MEASURED = {
     # profiles/partition_kernel_v2lite_32k.md
-    ("v2lite_32k", "190904b6c775"): dict(fetch_kib=18628.6, write_kib=8208.0, mfma_busy=0.021),
+    ("v2lite_32k", "35cfabb12306"): dict(fetch_kib=18630.0, write_kib=8208.0, mfma_busy=0.020),
     # profiles/wide_kernel_v3_131k.md
-    ("v3_131k", "0b25062740f2"): dict(fetch_kib=74494.7, write_kib=32832.0, mfma_busy=0.283),
+    ("v3_131k", "1cba2bacb378"): dict(fetch_kib=74491.7, write_kib=32832.0, mfma_busy=0.285),
 }
 
 

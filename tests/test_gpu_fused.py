@@ -33,6 +33,8 @@ FUSED_WORKLOADS = [
     ("v2lite_32k", dict(force_partitions=1, force_splits=1)),   # single pass: no merge
     ("two_req_32k_32k", {}),
     ("two_req_32k_20k", {}),
+    # 8 requests x 128 heads as eight 16-head groups each, bounded workspace.
+    ("mixed_b8", dict(heads_per_wg=16, workspace_limit_bytes=64 << 20)),
 ]
 
 
