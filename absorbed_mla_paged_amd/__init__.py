@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libmla_decode.so")
 
 MLA_F16, MLA_BF16 = 0, 1
 KV_LORA_RANK, ROPE_DIM, BLOCK_SIZE = 512, 64, 32
+BLOCK_SIZES = (16, 32)   # cache block sizes the kernels are built for
 FUSED_SYNC_BYTES_PER_REQUEST = 512
 STATUS = {0: "MLA_OK", -1: "MLA_E_NULL", -2: "MLA_E_SHAPE", -3: "MLA_E_RANGE",
           -4: "MLA_E_ALIGN", -5: "MLA_E_WORKSPACE", -6: "MLA_E_UNSUPPORTED",
@@ -77,13 +78,13 @@ def load_library(path: str | None = None):
     lib.mla_choose_partitions.restype = ctypes.c_int
     lib.mla_partition_range.argtypes = [i32, i32, i32, i32, i32, i32, pi32, pi32]
     lib.mla_partition_range.restype = ctypes.c_int
-    lib.mla_decode_partition.argtypes = [vp, vp, vp, vp, i32, vp, i32, vp, i32, i32, i32,
+    lib.mla_decode_partition.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, vp, i32, i32, i32,
                                          ctypes.c_float, i32, vp, vp, vp, i32, i32, i32,
                                          vp, vp, vp, vp, vp, vp]
     lib.mla_decode_partition.restype = ctypes.c_int
     lib.mla_decode_reduce.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
     lib.mla_decode_reduce.restype = ctypes.c_int
-    lib.mla_decode_fused.argtypes = [vp, vp, vp, vp, i32, vp, i32, vp, i32, i32, i32,
+    lib.mla_decode_fused.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, vp, i32, i32, i32,
                                      ctypes.c_float, i32, vp, vp, vp, i32, i32, i32,
                                      vp, vp, vp, vp, vp, vp, vp]
     lib.mla_decode_fused.restype = ctypes.c_int
@@ -227,13 +228,14 @@ def mla_decode_partition(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, co
                          out, lse2_out=None, debug_ranges=None, stream=None, q_len=None):
     """Launch the partition kernel (see include/mla_decode.h). q_absorbed is
     [B, H, 512], or [B, q_len, H, 512] / [B, q_len*H, 512] for several new
-    tokens per request."""
+    tokens per request. The cache block size is ckv_cache.shape[1] (16 or
+    32), and must be the one the plan was chosen for."""
     lib = load_library()
     _need_cuda(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens)
     B, H, Q = _query_shape(q_absorbed, q_len)
     _check(lib.mla_decode_partition(
         _ptr(q_absorbed), _ptr(q_pe), _ptr(ckv_cache), _ptr(kpe_cache), int(ckv_cache.shape[0]),
-        _ptr(block_table), int(block_table.shape[1]), _ptr(context_lens), B, H, Q,
+        int(ckv_cache.shape[1]), _ptr(block_table), int(block_table.shape[1]), _ptr(context_lens), B, H, Q,
         float(scale), _dtype_code(q_absorbed), _ptr(partitions), _ptr(splits), _ptr(row_indptr),
         int(total_rows), int(max_rows_per_req), int(heads_per_wg), _ptr(partial_out),
         _ptr(partial_lse2), _ptr(out), _ptr(lse2_out), _ptr(debug_ranges), _stream(stream)))
@@ -249,7 +251,7 @@ def mla_decode_fused(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, contex
     B, H, Q = _query_shape(q_absorbed, q_len)
     _check(lib.mla_decode_fused(
         _ptr(q_absorbed), _ptr(q_pe), _ptr(ckv_cache), _ptr(kpe_cache), int(ckv_cache.shape[0]),
-        _ptr(block_table), int(block_table.shape[1]), _ptr(context_lens), B, H, Q,
+        int(ckv_cache.shape[1]), _ptr(block_table), int(block_table.shape[1]), _ptr(context_lens), B, H, Q,
         float(scale), _dtype_code(q_absorbed), _ptr(partitions), _ptr(splits), _ptr(row_indptr),
         int(total_rows), int(max_rows_per_req), int(heads_per_wg), _ptr(partial_out),
         _ptr(partial_lse2), _ptr(out), _ptr(lse2_out), _ptr(sync), _ptr(debug_ranges),
@@ -289,13 +291,15 @@ class DecodePlan:
     """A chooser result with its arrays and workspace on the device."""
 
     def __init__(self, context_lens, num_heads: int, params: PlanParams | None = None,
-                 device="cuda", q_len: int = 1):
+                 device="cuda", q_len: int = 1, block_size: int = BLOCK_SIZE):
         import torch
         ctx = [int(c) for c in context_lens]
         self.batch = len(ctx)
         self.heads = num_heads
         self.q_len = int(q_len)
-        self.info = mla_choose_partitions(self.batch, num_heads, q_len, ctx, params)
+        self.block_size = int(block_size)
+        self.info = mla_choose_partitions(self.batch, num_heads, q_len, ctx, params,
+                                          block_size=self.block_size)
         i32 = torch.int32
         self.partitions = torch.tensor(self.info["P"], dtype=i32, device=device)
         self.splits = torch.tensor(self.info["S"], dtype=i32, device=device)
@@ -322,6 +326,9 @@ def decode(plan: DecodePlan, q_absorbed, q_pe, ckv_cache, kpe_cache, block_table
            scale: float, out, lse2_out=None, debug_ranges=None, stream=None, fused=False):
     """Partition launch, then the reduce launch when the plan needs one; with
     fused=True, one launch that merges too."""
+    if int(ckv_cache.shape[1]) != plan.block_size:
+        raise MlaError(-2, f"cache blocks of {int(ckv_cache.shape[1])} tokens, plan chosen for "
+                           f"{plan.block_size}")
     if fused:
         mla_decode_fused(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens, scale,
                          plan.partitions, plan.splits, plan.row_indptr, plan.total_rows,

@@ -25,7 +25,10 @@ struct TileRange {
   int64_t blk_lo, blk_hi;  // blocks [blk_lo, blk_hi) of the request
   int64_t tok_lo, tok_hi;  // tokens [tok_lo, tok_hi)
 };
-// The index math of mla_partition_range (host copy; the kernel has its own).
-TileRange tile_range(int64_t n, int32_t P, int32_t S, int32_t p, int32_t s);
+// Cache block sizes the kernels are built for: 32 and 16 tokens.
+bool valid_block_size(int32_t bs);
+// The index math of mla_partition_range (host copy; the kernel has its own),
+// for a context of n tokens in blocks of bs tokens.
+TileRange tile_range(int64_t n, int32_t bs, int32_t P, int32_t S, int32_t p, int32_t s);
 
 }  // namespace mla

@@ -10,8 +10,10 @@
 // into `out` when the request is a single row.
 //
 // Mapping onto one CU: 512 threads = 8 wave64, two per SIMD.
-//  * Stages: the row is cut into stages of two 32-token cache blocks
-//    (64 KB of ckv + 8 KB of kpe), held in two alternating LDS slots.
+//  * Stages: the row is cut into stages of 64 tokens (two 32-token cache
+//    blocks, or four of 16: 64 KB of ckv + 8 KB of kpe), held in two
+//    alternating LDS slots. The cache block size PG is a template
+//    parameter; it changes only the index math and the table lookups.
 //  * Copy waves (4..7) move stages in with global_load_lds_dwordx4 (16 B per
 //    lane, one 1 KB row per instruction, so whole 128 B lines). Once the
 //    memory queue of the CU is full, issuing a copy blocks the issuing wave;
@@ -56,7 +58,7 @@ namespace {
 using namespace dev;
 using namespace part;
 
-constexpr int ST_TOK = 2 * BS;                  // tokens per stage
+constexpr int ST_TOK = 2 * SEG;                 // tokens per stage
 constexpr int ST_KPE = ST_TOK * CKV_ROW;        // kpe rows after the ckv rows
 constexpr int STAGE = ST_TOK * (CKV_ROW + KPE_ROW);   // 72 KB
 constexpr int CWAVES = 4;                       // compute waves
@@ -76,7 +78,7 @@ static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 // The leading scalar kernel arguments (16 dwords, up to block_table) are
 // preloaded into SGPRs at wave launch on gfx950, so finding the row costs
 // no argument fetch; the PartitionArgs block is fetched meanwhile.
-template <int DT, bool FUSED>
+template <int DT, bool FUSED, int PG>
 __global__ __launch_bounds__(THREADS) void partition_kernel(
     int32_t groups, int32_t rows_per_req, int32_t slots, int32_t flags, int32_t total_rows,
     int32_t max_blocks, const int32_t* __restrict__ context_lens,
@@ -139,7 +141,7 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
     S = max(1, min(sv, 1 << 25));
     row = r0 + x;
   }
-  n = max(0, min(n, max_blocks * BS));
+  n = max(0, min(n, max_blocks * PG));
   if (x >= nrows || row < 0 || row >= total_rows) return;
   if constexpr (FUSED) {
     if (tid == 0)
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
   const int p = x / S;
   const int s = x % S;
   // Index math of mla_partition_range (must agree bit for bit).
-  const int nblk = cdiv(n, BS);
+  const int nblk = cdiv(n, PG);
   const int bpp = cdiv(nblk, P);
   const int pb0 = min(p * bpp, nblk);
   const int pb1 = min((p + 1) * bpp, nblk);
@@ -156,14 +158,15 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
   const int bps = m > 0 ? cdiv(m, S) : 0;
   const int blk_lo = (p < P) ? pb0 + min(s * bps, m) : nblk;
   const int blk_hi = (p < P) ? pb0 + min((s + 1) * bps, m) : nblk;
-  const int tok_lo = min(blk_lo * BS, n);
-  const int tok_end = min(blk_hi * BS, n);   // the row's range
+  const int tok_lo = min(blk_lo * PG, n);
+  const int tok_end = min(blk_hi * PG, n);   // the row's range
   // With several new tokens per request, this head group belongs to one new
   // token, which does not see the last hidden_tail() tokens of the context.
   const int n_vis = max(0, n - hidden_tail(flags, head0));
   const int tok_hi = max(tok_lo, min(tok_end, n_vis));
-  const int nblocks = cdiv(tok_hi - tok_lo, BS);   // non-empty blocks
-  const int nst = cdiv(nblocks, 2);                 // stages
+  constexpr int NPG = ST_TOK / PG;                 // cache blocks per stage
+  const int nblocks = cdiv(tok_hi - tok_lo, PG);   // non-empty cache blocks
+  const int nst = cdiv(nblocks, NPG);               // stages
 
   // LDS counters, zeroed behind one barrier (it waits for the scalar loads
   // above, never for Q or the table).
@@ -261,44 +264,45 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
     const char* ckv_base = reinterpret_cast<const char*>(a.ckv);
     const char* kpe_base = reinterpret_cast<const char*>(a.kpe);
     const uint32_t base = lds_addr(smem) + slot * STAGE;
-    // Physical blocks of stage k (a one-block stage copies its block twice,
-    // an L2 hit; its second half is never read). Looked up one stage
-    // ahead, so the block-table round trip overlaps the waits below.
+    // Physical blocks of stage k (a stage with fewer cache blocks than
+    // NPG copies its last block again, an L2 hit; those rows are either
+    // never read or zeroed below). Looked up one stage ahead, so the
+    // block-table round trip overlaps the waits below.
     auto lookup = [&](int k, int64_t* ph) {
-      const int nb_here = min(2, nblocks - 2 * k);
+      const int nb_here = min(NPG, nblocks - NPG * k);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int blk = blk_lo + 2 * k + min(j, nb_here - 1);
+      for (int j = 0; j < NPG; ++j) {
+        const int blk = blk_lo + NPG * k + min(j, nb_here - 1);
         const int v = __builtin_amdgcn_readfirstlane(load_const(block_table, tbl0 + blk));
         ph[j] = (int64_t)max(0, min(v, last_blk));
       }
     };
-    int64_t phys[2], phys_next[2] = {0, 0};
+    int64_t phys[NPG], phys_next[NPG] = {};
     if (slot < nst) lookup(slot, phys_next);
     for (int k = slot, g = 0; k < nst; k += 2, ++g) {
-      phys[0] = phys_next[0];
-      phys[1] = phys_next[1];
+#pragma unroll
+      for (int j = 0; j < NPG; ++j) phys[j] = phys_next[j];
       if (k + 2 < nst) lookup(k + 2, phys_next);
       wait_counter(freed + slot, CWAVES * g);
       // Stages are issued in order, so the memory queue returns them in
       // order and stage k can be computed while stage k + 1 is arriving.
       wait_counter(issued, 2 * k);
-      // ops 0..63: ckv rows (block op / 32, row op % 32); 64..71: kpe rows
-      // 8 (op - 64) .. + 8 of the stage.
+      // ops 0..63: ckv row op of the stage (cache block op / PG, row
+      // op % PG); 64..71: kpe rows 8 (op - 64) .. + 8 of the stage.
 #pragma unroll
       for (int i = 0; i < OPS_PER_COPY; ++i) {
         const int op = half * OPS_PER_COPY + i;
-        if (op < 64) {
-          const int j = op >> 5, r = op & 31;
-          const int chunk = (lane & ~15) | ((lane & 15) ^ swz_ckv(r));
-          dma16(ckv_base + phys[j] * (BS * CKV_ROW) + r * CKV_ROW + chunk * 16,
-                base + (j * BS + r) * CKV_ROW);
+        if (op < ST_TOK) {
+          const int j = op / PG, r = op % PG;
+          const int chunk = (lane & ~15) | ((lane & 15) ^ swz_ckv(op));
+          dma16(ckv_base + phys[j] * (PG * CKV_ROW) + r * CKV_ROW + chunk * 16,
+                base + op * CKV_ROW);
         } else {
-          const int t8 = op - 64;
-          const int j = t8 >> 2;
-          const int r = (t8 & 3) * 8 + (lane >> 3);
-          const int chunk = (lane & 7) ^ swz_kpe(r);
-          dma16(kpe_base + phys[j] * (BS * KPE_ROW) + r * KPE_ROW + chunk * 16,
+          const int t8 = op - ST_TOK;
+          const int sr = t8 * 8 + (lane >> 3);   // row of the stage
+          const int j = (t8 * 8) / PG;            // the 8 rows share a cache block
+          const int chunk = (lane & 7) ^ swz_kpe(sr);
+          dma16(kpe_base + phys[j] * (PG * KPE_ROW) + (sr % PG) * KPE_ROW + chunk * 16,
                 base + ST_KPE + t8 * 1024);
         }
       }
@@ -308,9 +312,9 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
       if (valid < ST_TOK) {
         // Rows past the context end may hold anything (NaN included): zero
         // the latent values of the ones this wave brought in, so that
-        // 0-probability tokens add exactly 0. A one-block stage never reads
-        // rows 32..63.
-        const int zend = min(valid <= BS ? BS : ST_TOK, half ? 64 : 36);
+        // 0-probability tokens add exactly 0. A stage of at most 32 tokens
+        // never reads rows 32..63.
+        const int zend = min(valid <= SEG ? SEG : ST_TOK, half ? 64 : 36);
         const int zbeg = max(valid, half ? 36 : 0);
         for (int idx = lane; idx < (zend - zbeg) * (CKV_ROW / 16); idx += 64) {
           const int r = zbeg + idx / (CKV_ROW / 16);
@@ -455,7 +459,7 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
     // K-step (its second half is never read).
     constexpr int VD = 7;   // fragments in flight: 2 VD <= 15
     auto vaddr = [&](int f) {
-      return sbase + voff + (f >> 3) * (BS * CKV_ROW) + 32u * (uint32_t)((f & 7) ^ vsh);
+      return sbase + voff + (f >> 3) * (SEG * CKV_ROW) + 32u * (uint32_t)((f & 7) ^ vsh);
     };
     u32x2 vr[2 * DT_PER_WAVE][2];
 #pragma unroll
@@ -499,7 +503,7 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    if (valid > BS) values(std::integral_constant<int, 2 * DT_PER_WAVE>{});
+    if (valid > SEG) values(std::integral_constant<int, 2 * DT_PER_WAVE>{});
     else values(std::integral_constant<int, DT_PER_WAVE>{});
     bump_counter(freed + slot, lane);
   }
@@ -538,7 +542,8 @@ namespace {
 
 // Checks and launch shared by mla_decode_partition and mla_decode_fused.
 int partition_launch(bool fused, const void* q_absorbed, const void* q_pe, const void* ckv_cache,
-                     const void* kpe_cache, int32_t num_blocks, const int32_t* block_table,
+                     const void* kpe_cache, int32_t num_blocks, int32_t block_size,
+                     const int32_t* block_table,
                      int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch,
                      int32_t num_heads, int32_t q_len, float scale, int32_t dtype,
                      const int32_t* partitions,
@@ -558,6 +563,8 @@ int partition_launch(bool fused, const void* q_absorbed, const void* q_pe, const
   if (!valid_heads_per_wg(num_heads, hpw))
     return fail(MLA_E_UNSUPPORTED, "heads_per_wg %d for %d heads (16 or 64 dividing it)",
                 hpw, num_heads);
+  if (!valid_block_size(block_size))
+    return fail(MLA_E_UNSUPPORTED, "block_size %d (16 or 32 are supported)", block_size);
   if (!std::isfinite(scale)) return fail(MLA_E_RANGE, "scale is not finite");
   if (batch == 0) return MLA_OK;
   if (!q_absorbed || !q_pe || !ckv_cache || !kpe_cache || !block_table || !context_lens)
@@ -622,17 +629,24 @@ int partition_launch(bool fused, const void* q_absorbed, const void* q_pe, const
   const dim3 grid((unsigned)wgs), block(THREADS);
   const int32_t dflag = part::pack_flags(direct, q_len, num_heads), sl = (int32_t)slots;
   if (hpw != HG)
-    part::launch_wide(dtype, hpw, (unsigned)wgs, stream, groups, rows_per_req, sl, dflag,
+    part::launch_wide(dtype, block_size, (unsigned)wgs, stream, groups, rows_per_req, sl, dflag,
                       total_rows, max_blocks_per_seq, context_lens, row_indptr, partitions,
                       splits, block_table, a);
 #define MLA_LAUNCH(K)                                                                        \
   hipLaunchKernelGGL(K, grid, block, 0, stream, groups, rows_per_req, sl, dflag, total_rows, \
                      max_blocks_per_seq, context_lens, row_indptr, partitions, splits,       \
                      block_table, a)
-  else if (dtype == MLA_F16 && merge_here) MLA_LAUNCH((partition_kernel<0, true>));
-  else if (dtype == MLA_F16) MLA_LAUNCH((partition_kernel<0, false>));
-  else if (merge_here) MLA_LAUNCH((partition_kernel<1, true>));
-  else MLA_LAUNCH((partition_kernel<1, false>));
+  else if (block_size == 16) {
+    if (dtype == MLA_F16 && merge_here) MLA_LAUNCH((partition_kernel<0, true, 16>));
+    else if (dtype == MLA_F16) MLA_LAUNCH((partition_kernel<0, false, 16>));
+    else if (merge_here) MLA_LAUNCH((partition_kernel<1, true, 16>));
+    else MLA_LAUNCH((partition_kernel<1, false, 16>));
+  } else {
+    if (dtype == MLA_F16 && merge_here) MLA_LAUNCH((partition_kernel<0, true, 32>));
+    else if (dtype == MLA_F16) MLA_LAUNCH((partition_kernel<0, false, 32>));
+    else if (merge_here) MLA_LAUNCH((partition_kernel<1, true, 32>));
+    else MLA_LAUNCH((partition_kernel<1, false, 32>));
+  }
 #undef MLA_LAUNCH
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(MLA_E_HIP, "partition launch: %s", hipGetErrorString(e));
@@ -645,14 +659,16 @@ int partition_launch(bool fused, const void* q_absorbed, const void* q_pe, const
 
 extern "C" int mla_decode_partition(
     const void* q_absorbed, const void* q_pe, const void* ckv_cache, const void* kpe_cache,
-    int32_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
+    int32_t num_blocks, int32_t block_size, const int32_t* block_table,
+    int32_t max_blocks_per_seq,
     const int32_t* context_lens, int32_t batch, int32_t num_heads, int32_t q_len, float scale,
     int32_t dtype,
     const int32_t* partitions, const int32_t* splits, const int32_t* row_indptr,
     int32_t total_rows, int32_t max_rows_per_req, int32_t heads_per_wg, float* partial_out,
     float* partial_lse2, void* out, float* lse2_out, int32_t* debug_ranges,
     hipStream_t stream) {
-  return partition_launch(false, q_absorbed, q_pe, ckv_cache, kpe_cache, num_blocks, block_table,
+  return partition_launch(false, q_absorbed, q_pe, ckv_cache, kpe_cache, num_blocks, block_size,
+                          block_table,
                           max_blocks_per_seq, context_lens, batch, num_heads, q_len, scale, dtype,
                           partitions, splits, row_indptr, total_rows, max_rows_per_req,
                           heads_per_wg, partial_out, partial_lse2, out, lse2_out, nullptr,
@@ -661,14 +677,16 @@ extern "C" int mla_decode_partition(
 
 extern "C" int mla_decode_fused(
     const void* q_absorbed, const void* q_pe, const void* ckv_cache, const void* kpe_cache,
-    int32_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
+    int32_t num_blocks, int32_t block_size, const int32_t* block_table,
+    int32_t max_blocks_per_seq,
     const int32_t* context_lens, int32_t batch, int32_t num_heads, int32_t q_len, float scale,
     int32_t dtype,
     const int32_t* partitions, const int32_t* splits, const int32_t* row_indptr,
     int32_t total_rows, int32_t max_rows_per_req, int32_t heads_per_wg, float* partial_out,
     float* partial_lse2, void* out, float* lse2_out, uint64_t* sync, int32_t* debug_ranges,
     hipStream_t stream) {
-  return partition_launch(true, q_absorbed, q_pe, ckv_cache, kpe_cache, num_blocks, block_table,
+  return partition_launch(true, q_absorbed, q_pe, ckv_cache, kpe_cache, num_blocks, block_size,
+                          block_table,
                           max_blocks_per_seq, context_lens, batch, num_heads, q_len, scale, dtype,
                           partitions, splits, row_indptr, total_rows, max_rows_per_req,
                           heads_per_wg, partial_out, partial_lse2, out, lse2_out, sync,

@@ -44,7 +44,11 @@ __device__ __forceinline__ int hidden_tail(int32_t flags, int head0) {
 }
 #endif
 
-constexpr int BS = MLA_BLOCK_SIZE;      // tokens per cache block
+// Tokens per segment: one K-step of the value product and one LDS ring slot
+// of the wide kernel. A segment is one cache block of 32 tokens or two of
+// 16; the kernels are templates on the cache block size PG (16 or 32),
+// which enters only the index math and the block-table lookups.
+constexpr int SEG = 32;
 constexpr int LAT = MLA_KV_LORA_RANK;   // 512
 constexpr int ROPE = MLA_ROPE_DIM;      // 64
 constexpr int CKV_ROW = LAT * 2;        // bytes per ckv row
@@ -67,8 +71,8 @@ struct RowInfo {
   int hg;       // head group
   int tok_lo, tok_hi;   // tokens this head group sees in the row
   int tok_end;          // end of the row's range itself (for debug_ranges)
-  int blk_lo;   // first block of the range (request-local)
-  int nblocks;  // blocks holding at least one visible token
+  int blk_lo;   // first cache block of the range (request-local)
+  int nseg;     // 32-token segments holding at least one visible token
 };
 
 // Which (request, local row, head group) workgroup L owns. Workgroups are
@@ -88,10 +92,12 @@ __device__ __forceinline__ bool slot_of(int L, int groups, int rows_per_req, int
 }
 
 // Row metadata in one round of scalar loads, then the index math of
-// mla_partition_range (must agree with it bit for bit). The row's range is
+// mla_partition_range for cache blocks of PG tokens (must agree with it bit
+// for bit). The row's range is
 // cut from the whole context; `hidden` more tokens at its end are masked for
 // this head group (new token j of a window of q_len sees all but the last
 // q_len - 1 - j).
+template <int PG>
 __device__ __forceinline__ bool find_row(int b, int x, int direct, int total_rows, int hidden,
                                          int max_blocks, const int32_t* context_lens,
                                          const int32_t* row_indptr,
@@ -110,11 +116,11 @@ __device__ __forceinline__ bool find_row(int b, int x, int direct, int total_row
     S = max(1, min(sv, 1 << 25));
     row = r0 + x;
   }
-  n = max(0, min(n, max_blocks * BS));
+  n = max(0, min(n, max_blocks * PG));
   if (x >= nrows || row < 0 || row >= total_rows) return false;
   const int p = x / S;
   const int s = x % S;
-  const int nblk = cdiv(n, BS);
+  const int nblk = cdiv(n, PG);
   const int bpp = cdiv(nblk, P);
   const int pb0 = min(p * bpp, nblk);
   const int pb1 = min((p + 1) * bpp, nblk);
@@ -125,11 +131,11 @@ __device__ __forceinline__ bool find_row(int b, int x, int direct, int total_row
   ri->b = b;
   ri->row = row;
   const int n_vis = max(0, n - hidden);
-  ri->tok_lo = min(blk_lo * BS, n);
-  ri->tok_end = min(blk_hi * BS, n);
+  ri->tok_lo = min(blk_lo * PG, n);
+  ri->tok_end = min(blk_hi * PG, n);
   ri->tok_hi = max(ri->tok_lo, min(ri->tok_end, n_vis));
   ri->blk_lo = blk_lo;
-  ri->nblocks = cdiv(ri->tok_hi - ri->tok_lo, BS);
+  ri->nseg = cdiv(ri->tok_hi - ri->tok_lo, SEG);
   return true;
 }
 
@@ -149,7 +155,7 @@ __device__ __forceinline__ void bump_counter(MLA_LDS uint32_t* c, int lane) {
 
 // Launch of the wide kernel (heads_per_wg 64); arguments as the 16-head
 // kernel's. Host side, after the launcher's checks.
-void launch_wide(int dtype, int hpw, unsigned wgs, hipStream_t stream, int32_t groups,
+void launch_wide(int dtype, int block_size, unsigned wgs, hipStream_t stream, int32_t groups,
                  int32_t rows_per_req, int32_t slots, int32_t flags, int32_t total_rows,
                  int32_t max_blocks, const int32_t* context_lens, const int32_t* row_indptr,
                  const int32_t* partitions, const int32_t* splits, const int32_t* block_table,

@@ -61,8 +61,8 @@ namespace {
 using namespace dev;
 
 constexpr int HPW = 64;                         // heads per workgroup
-constexpr int SLOT = BS * (CKV_ROW + KPE_ROW);  // 36 KB per one-block slot
-constexpr int SLOT_KPE = BS * CKV_ROW;          // kpe rows after the ckv rows
+constexpr int SLOT = SEG * (CKV_ROW + KPE_ROW); // 36 KB per one-block slot
+constexpr int SLOT_KPE = SEG * CKV_ROW;         // kpe rows after the ckv rows
 constexpr int NSLOT = 4;
 // The value waves copy blocks 0 and 1 before the first step and block
 // i + 2 right after the meeting of step i, into the slot of block i - 2.
@@ -72,7 +72,7 @@ constexpr int THREADS = 64 * WAVES;
 constexpr int NSC = 4;                          // score waves (0..3)
 constexpr int DT_WAVE = LAT / 16 / 4;           // 8 output dim tiles per value wave
 constexpr int HT_ALL = HPW / 16;                // 4 head tiles per workgroup
-constexpr int OPS = BS + BS * KPE_ROW / 1024;   // 36 copy instructions per block
+constexpr int OPS = SEG + SEG * KPE_ROW / 1024; // 36 copy instructions per block
 constexpr int OPW = OPS / 4;                    // 9 per value wave
 constexpr int XP = NSLOT * SLOT;                // probabilities [parity][wave][lane] 16 B
 constexpr int XM = XP + 2 * NSC * 64 * 16;      // per-head floats [wave][2][16]
@@ -112,6 +112,12 @@ template <> struct Prob<1> {
   }
 };
 
+// Physical cache blocks holding one 32-token segment (both entries equal
+// when the cache block is 32 tokens).
+struct Phys {
+  int64_t p[2];
+};
+
 // Wait until at most `later` blocks' worth of this wave's copies are still
 // in flight (copies complete in issue order).
 __device__ __forceinline__ void wait_blocks(int later) {
@@ -131,7 +137,9 @@ __device__ __forceinline__ void meet() {
   asm volatile("" ::: "memory");
 }
 
-template <int DT>
+// A "block" below is one 32-token segment of the row: one cache block of
+// PG = 32 tokens, or two of PG = 16 (looked up separately in the table).
+template <int DT, int PG>
 __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
     int32_t groups, int32_t rows_per_req, int32_t slots, int32_t flags, int32_t total_rows,
     int32_t max_blocks, const int32_t* __restrict__ context_lens,
@@ -163,11 +171,11 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
 
   const int direct = flags & 1;
   RowInfo ri;
-  if (!find_row(b, x, direct, total_rows, hidden_tail(flags, hwg), max_blocks, context_lens,
+  if (!find_row<PG>(b, x, direct, total_rows, hidden_tail(flags, hwg), max_blocks, context_lens,
                 row_indptr, partitions, splits, &ri))
     return;
   const int row = ri.row;
-  const int nblocks = ri.nblocks;
+  const int nblocks = ri.nseg;   // 32-token blocks of the row
   // Output of value-wave lane (ln, lg) for head tile ht (head hwg + 16 ht +
   // ln) and dim tile dt (dims 16 dt + 4 lg .. + 4).
   auto store = [&](int ht, int dt, f32x4 v) {
@@ -213,28 +221,48 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
   const char* ckv_base = reinterpret_cast<const char*>(a.ckv);
   const char* kpe_base = reinterpret_cast<const char*>(a.kpe);
   const uint32_t lds0 = lds_addr(smem);
+  // Physical cache blocks of 32-token block k: with PG = 16 its two
+  // halves, the second clamped to the row's last cache block with a token
+  // (a half-filled last block reads its first half twice; rows past the end
+  // are zeroed before use). With PG = 32 both are the one block.
+  const int last_page = cdiv(ntok_all, PG) - 1;
   auto phys_of = [&](int k) {
-    const int v = __builtin_amdgcn_readfirstlane(load_const(block_table, tbl0 + k));
-    return (int64_t)max(0, min(v, last_phys));
+    Phys ph;
+    const int c0 = k * (SEG / PG);
+    const int v0 = __builtin_amdgcn_readfirstlane(load_const(block_table, tbl0 + c0));
+    ph.p[0] = (int64_t)max(0, min(v0, last_phys));
+    if constexpr (PG == SEG) {
+      ph.p[1] = ph.p[0];
+    } else {
+      const int c1 = min(c0 + 1, last_page);
+      const int v1 = __builtin_amdgcn_readfirstlane(load_const(block_table, tbl0 + c1));
+      ph.p[1] = (int64_t)max(0, min(v1, last_phys));
+    }
+    return ph;
   };
   // Value wave sw's quarter of block k's copies into slot k % 4: copy i is
   // op 9 sw + i; ops 0..31 are ckv rows, 32..35 kpe rows 8 (op - 32) .. + 8.
   // Chunk c of an LDS row sits at position c ^ swizzle(row).
-  auto issue_one = [&](int k, int64_t phys, int i) {
+  auto issue_one = [&](int k, const Phys& ph, int i) {
     const uint32_t base = lds0 + (k & (NSLOT - 1)) * SLOT;
     const int op = sw * OPW + i;
     // The lane offsets are recomputed per copy from an opaque lane index:
     // hoisted out of the step loop they would hold registers throughout it.
     int lane;
     asm volatile("v_mov_b32 %0, %1" : "=v"(lane) : "v"(lane_id));
-    if (op < BS) {
+    if (op < SEG) {
+      // ckv row op: row op % PG of cache block op / PG of the segment.
       const uint32_t voff = ((lane & ~15) | ((lane & 15) ^ swz_ckv(op))) * 16;
-      dma16s(voff, ckv_base + phys * (BS * CKV_ROW) + op * CKV_ROW, base + op * CKV_ROW);
+      const int64_t pj = (PG == SEG || op < PG) ? ph.p[0] : ph.p[1];   // wave-uniform
+      dma16s(voff, ckv_base + pj * (PG * CKV_ROW) + (op % PG) * CKV_ROW, base + op * CKV_ROW);
     } else {
-      const int t8 = op - BS;
+      // kpe rows 8 t8 .. + 8, all in one cache block.
+      const int t8 = op - SEG;
       const int r = t8 * 8 + (lane >> 3);
       const uint32_t voff = (lane >> 3) * KPE_ROW + ((lane & 7) ^ swz_kpe(r)) * 16;
-      dma16s(voff, kpe_base + phys * (BS * KPE_ROW) + t8 * 1024, base + SLOT_KPE + t8 * 1024);
+      const int64_t pj = (PG == SEG || t8 * 8 < PG) ? ph.p[0] : ph.p[1];
+      dma16s(voff, kpe_base + pj * (PG * KPE_ROW) + ((t8 * 8) % PG) * KPE_ROW,
+             base + SLOT_KPE + t8 * 1024);
     }
   };
 
@@ -242,9 +270,9 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
   // own copies of the last block have landed, a wave zeroes the ckv rows it
   // brought in, so that 0-probability tokens add exactly 0.
   auto zero_tail = [&](int k) {
-    const int valid = min(BS, ntok_all - k * BS);
-    if (valid < BS) {
-      for (int r = max(valid, sw * OPW); r < min(BS, (sw + 1) * OPW); ++r)
+    const int valid = min(SEG, ntok_all - k * SEG);
+    if (valid < SEG) {
+      for (int r = max(valid, sw * OPW); r < min(SEG, (sw + 1) * OPW); ++r)
         *(MLA_LDS u32x4*)(smem + (k & (NSLOT - 1)) * SLOT + r * CKV_ROW + lane * 16) =
             u32x4{0u, 0u, 0u, 0u};
     }
@@ -253,9 +281,9 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
   // During step i the value waves fetch block i + 2 into the slot of block
   // i - 2, free since the step's meeting. `next` holds the block table entry
   // of the following refill, read one step ahead.
-  auto refill = [&](int i, int64_t& next) {
+  auto refill = [&](int i, Phys& next) {
     if (i + 2 >= NPRO && i + 2 < nblocks) {
-      const int64_t ph = next;
+      const Phys ph = next;
       if (i + 3 < nblocks) next = phys_of(i + 3);
 #pragma unroll
       for (int c = 0; c < OPW; ++c) issue_one(i + 2, ph, c);
@@ -369,7 +397,7 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
         if (i >= nblocks) continue;
         // ---- scores: my 16 tokens x 32 heads of block i -----------------------
         const uint32_t sbase = lds0 + (i & (NSLOT - 1)) * SLOT;
-        const int valid = min(BS, ntok - i * BS);
+        const int valid = min(SEG, ntok - i * SEG);
         auto kaddr = [&](int ks) {
           return sbase + ((ks < LAT / 32) ? offs_k[ks & 3] + 256 * (ks >> 2)
                                           : offs_p[ks - LAT / 32]);
@@ -401,7 +429,7 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) sc[j][e] = sv[e];
         }
-        if (valid < BS) {   // the row's last block: hide tokens past its end
+        if (valid < SEG) {   // the row's last block: hide tokens past its end
 #pragma unroll
           for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -546,7 +574,7 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
     // Blocks 0 and 1 before the first step (the rest during the steps).
     const int npro = min(NPRO, nblocks);
     for (int k = 0; k < npro; ++k) {
-      const int64_t ph = phys_of(k);
+      const Phys ph = phys_of(k);
 #pragma unroll
       for (int c = 0; c < OPW; ++c) issue_one(k, ph, c);
     }
@@ -557,7 +585,7 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
     // Start of step i: block i must be in LDS (my later copies, of blocks
     // i + 1 .. last, may still be in flight), then M_step(i), then the copy
     // of block i + 2.
-    int64_t phys_next = nblocks > NPRO ? phys_of(NPRO) : 0;
+    Phys phys_next = nblocks > NPRO ? phys_of(NPRO) : Phys{{0, 0}};
     auto step_begin = [&](int i) {
       if (i < nblocks) {
         const int last = min(max(npro - 1, i + 1), nblocks - 1);
@@ -596,20 +624,16 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
 
 }  // namespace
 
-void launch_wide(int dtype, int hpw, unsigned wgs, hipStream_t stream, int32_t groups,
+void launch_wide(int dtype, int block_size, unsigned wgs, hipStream_t stream, int32_t groups,
                  int32_t rows_per_req, int32_t slots, int32_t flags, int32_t total_rows,
                  int32_t max_blocks, const int32_t* context_lens, const int32_t* row_indptr,
                  const int32_t* partitions, const int32_t* splits, const int32_t* block_table,
                  const PartitionArgs& a) {
-  (void)hpw;  // 64: the only wide layout
-  if (dtype == MLA_F16)
-    hipLaunchKernelGGL(wide_kernel<0>, dim3(wgs), dim3(THREADS), 0, stream, groups, rows_per_req,
-                       slots, flags, total_rows, max_blocks, context_lens, row_indptr,
-                       partitions, splits, block_table, a);
-  else
-    hipLaunchKernelGGL(wide_kernel<1>, dim3(wgs), dim3(THREADS), 0, stream, groups, rows_per_req,
-                       slots, flags, total_rows, max_blocks, context_lens, row_indptr,
-                       partitions, splits, block_table, a);
+  auto kernel = dtype == MLA_F16 ? (block_size == 16 ? wide_kernel<0, 16> : wide_kernel<0, 32>)
+                                 : (block_size == 16 ? wide_kernel<1, 16> : wide_kernel<1, 32>);
+  hipLaunchKernelGGL(kernel, dim3(wgs), dim3(THREADS), 0, stream, groups, rows_per_req, slots,
+                     flags, total_rows, max_blocks, context_lens, row_indptr, partitions, splits,
+                     block_table, a);
 }
 
 }  // namespace part

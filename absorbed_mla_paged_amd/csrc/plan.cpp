@@ -52,8 +52,10 @@ bool valid_heads_per_wg(int32_t heads, int32_t hpw) {
   return (hpw == 16 || hpw == 64) && heads % hpw == 0;
 }
 
-TileRange tile_range(int64_t n, int32_t P, int32_t S, int32_t p, int32_t s) {
-  const int64_t nblk = cdiv(n, MLA_BLOCK_SIZE);
+bool valid_block_size(int32_t bs) { return bs == MLA_BLOCK_SIZE || bs == MLA_BLOCK_SIZE_SMALL; }
+
+TileRange tile_range(int64_t n, int32_t bs, int32_t P, int32_t S, int32_t p, int32_t s) {
+  const int64_t nblk = cdiv(n, bs);
   const int64_t bpp = cdiv(nblk, P);
   const int64_t pb0 = std::min<int64_t>(p * bpp, nblk);
   const int64_t pb1 = std::min<int64_t>((p + 1) * bpp, nblk);
@@ -64,8 +66,8 @@ TileRange tile_range(int64_t n, int32_t P, int32_t S, int32_t p, int32_t s) {
   TileRange r;
   r.blk_lo = lo;
   r.blk_hi = hi;
-  r.tok_lo = std::min<int64_t>(lo * MLA_BLOCK_SIZE, n);
-  r.tok_hi = std::min<int64_t>(hi * MLA_BLOCK_SIZE, n);
+  r.tok_lo = std::min<int64_t>(lo * bs, n);
+  r.tok_hi = std::min<int64_t>(hi * bs, n);
   return r;
 }
 
@@ -94,11 +96,11 @@ int mla_partition_range(int32_t ctx, int32_t block_size, int32_t P, int32_t S, i
                         int32_t s, int32_t* tok_begin, int32_t* tok_end) {
   clear_error();
   if (!tok_begin || !tok_end) return fail(MLA_E_NULL, "mla_partition_range: null output");
-  if (block_size != MLA_BLOCK_SIZE)
-    return fail(MLA_E_UNSUPPORTED, "block_size %d (only 32 is supported)", block_size);
+  if (!valid_block_size(block_size))
+    return fail(MLA_E_UNSUPPORTED, "block_size %d (16 or 32 are supported)", block_size);
   if (ctx < 0 || P < 1 || S < 1 || p < 0 || p >= P || s < 0 || s >= S)
     return fail(MLA_E_RANGE, "mla_partition_range: ctx=%d P=%d S=%d p=%d s=%d", ctx, P, S, p, s);
-  const TileRange r = tile_range(ctx, P, S, p, s);
+  const TileRange r = tile_range(ctx, block_size, P, S, p, s);
   *tok_begin = static_cast<int32_t>(r.tok_lo);
   *tok_end = static_cast<int32_t>(r.tok_hi);
   return MLA_OK;
@@ -116,8 +118,8 @@ int mla_choose_partitions(int32_t batch, int32_t num_heads, int32_t q_len,
   if (q_len < 1) return fail(MLA_E_SHAPE, "q_len %d < 1", q_len);
   if (q_len > MLA_MAX_QLEN)
     return fail(MLA_E_UNSUPPORTED, "q_len %d (at most %d)", q_len, MLA_MAX_QLEN);
-  if (block_size != MLA_BLOCK_SIZE)
-    return fail(MLA_E_UNSUPPORTED, "block_size %d (only 32 is supported)", block_size);
+  if (!valid_block_size(block_size))
+    return fail(MLA_E_UNSUPPORTED, "block_size %d (16 or 32 are supported)", block_size);
   if (num_heads < MLA_MIN_HEADS || num_heads > MLA_MAX_HEADS || num_heads % 16)
     return fail(MLA_E_UNSUPPORTED, "num_heads %d (need a multiple of 16 in [16, 128])", num_heads);
   if (batch > 0 && (!ctx || !P_out || !S_out)) return fail(MLA_E_NULL, "null per-request array");
@@ -151,7 +153,7 @@ int mla_choose_partitions(int32_t batch, int32_t num_heads, int32_t q_len,
   std::vector<int64_t> nblk(batch), P(batch), S(batch);
   int64_t total_blocks = 0;
   for (int32_t b = 0; b < batch; ++b) {
-    nblk[b] = cdiv(ctx[b], MLA_BLOCK_SIZE);
+    nblk[b] = cdiv(ctx[b], block_size);
     total_blocks += nblk[b];
   }
   const bool autoP = prm.force_partitions == 0;

@@ -52,6 +52,12 @@ MEASURED = {
 }
 
 
+def workload_key(name: str, block_size: int) -> str:
+    """Key of the recorded counters: the workload, and the block size when
+    it is not 32."""
+    return name if block_size == 32 else f"{name}@bs{block_size}"
+
+
 def kernel_hash(hpw: int) -> str:
     """Hash of the kernel's sources with comments and whitespace removed, so
     that recorded counters stay valid across documentation-only edits."""
@@ -82,7 +88,7 @@ def host_chooser_us(case, prm, calls: int = 2000) -> float:
     info = mla._PlanInfo()
     c_prm = prm._c() if prm is not None else None
     pp = ctypes.byref(c_prm) if c_prm is not None else None
-    args = (B, case.heads, case.q_len, ctx, 32, pp, P, S, ind, ctypes.byref(info))
+    args = (B, case.heads, case.q_len, ctx, case.block_size, pp, P, S, ind, ctypes.byref(info))
     fn = lib.mla_choose_partitions
     if fn(*args) != 0:
         raise RuntimeError(mla.mla_last_error())
@@ -191,6 +197,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="v2lite_32k")
     ap.add_argument("--single-pass", action="store_true", help="force P = S = 1")
+    ap.add_argument("--block-size", type=int, default=32, choices=(16, 32),
+                    help="tokens per cache block of the paged layout")
     ap.add_argument("--fused", action="store_true",
                     help="partition and merge in one launch (mla_decode_fused)")
     ap.add_argument("--projections", action="store_true",
@@ -225,7 +233,7 @@ def main():
     import mla_synth
 
     log(f"[bench] workload={args.workload} steps={args.steps} warmup={args.warmup}")
-    case = mla_synth.make_workload(args.workload)
+    case = mla_synth.make_workload(args.workload, block_size=args.block_size)
     if args.projections:
         projections(case, args, torch, mla)
         return
@@ -245,7 +253,8 @@ def main():
     table = torch.from_numpy(case.block_table).to(dev)
     ctx = torch.from_numpy(case.context_lens).to(dev)
     prm = mla.PlanParams(force_partitions=1, force_splits=1) if args.single_pass else None
-    plan = mla.DecodePlan(case.context_lens, case.heads, prm, device=dev, q_len=case.q_len)
+    plan = mla.DecodePlan(case.context_lens, case.heads, prm, device=dev, q_len=case.q_len,
+                          block_size=case.block_size)
     qrows = case.q_len * case.heads
     info = plan.info
     out = torch.empty((case.batch, qrows, 512), dtype=td, device=dev)
@@ -257,7 +266,8 @@ def main():
     def step(j):
         # Host chooser (same contexts every step, so the device plan arrays
         # already hold its answer), then the device work.
-        mla.mla_choose_partitions(case.batch, case.heads, case.q_len, case.context_lens, prm)
+        mla.mla_choose_partitions(case.batch, case.heads, case.q_len, case.context_lens, prm,
+                                  block_size=case.block_size)
         c, k = copies[j % ncopy]
         mla.decode(plan, qa, qp, c, k, table, ctx, case.scale, out, lse2, fused=args.fused)
 
@@ -328,7 +338,7 @@ def main():
     split_bytes = info["total_rows"] * qrows * 513 * 4 if info["needs_reduce"] else 0
     pair_gbs = alg["total"] / (ms_per_step * 1e-3) / 1e9
     khash = kernel_hash(info["heads_per_wg"])
-    meas = MEASURED.get((args.workload, khash))
+    meas = MEASURED.get((workload_key(args.workload, case.block_size), khash))
     traffic = None
     if meas is not None:
         traffic = int(round((meas["fetch_kib"] * FETCH_SCALE + meas["write_kib"] * WRITE_SCALE) * 1024))
@@ -359,7 +369,7 @@ def main():
         "config": {"workload": args.workload, "batch": case.batch, "heads": case.heads,
                    "q_len": case.q_len,
                    "context_lens": [int(n) for n in case.context_lens],
-                   "block_size": 32, "kv_lora_rank": 512, "rope_dim": 64,
+                   "block_size": case.block_size, "kv_lora_rank": 512, "rope_dim": 64,
                    "plan": {"P": info["P"], "S": info["S"], "rows": info["total_rows"]},
                    "single_pass": bool(args.single_pass), "kv_copies": ncopy},
         "device_us": round(device_ms * 1e3, 3),

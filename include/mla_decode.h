@@ -44,10 +44,14 @@ extern "C" {
 #endif
 
 /* Geometry fixed by the cache layout (vllm-metal pull request 601,
- * "Wrapper benchmark": kv_lora_rank 512, qk_rope_head_dim 64, block 32). */
+ * "Wrapper benchmark": kv_lora_rank 512, qk_rope_head_dim 64, block 32).
+ * Blocks of 16 tokens are also accepted (the "block16" layout that pull
+ * request's reviewer asks to see covered): block_size is 16 or 32 wherever
+ * an entry point takes it. */
 #define MLA_KV_LORA_RANK 512
 #define MLA_ROPE_DIM 64
 #define MLA_BLOCK_SIZE 32
+#define MLA_BLOCK_SIZE_SMALL 16
 #define MLA_MAX_PARTITIONS 8     /* "2 to 8 partitions" (same page, "What changed") */
 #define MLA_MAX_SPLITS 4096
 #define MLA_MIN_HEADS 16
@@ -88,7 +92,7 @@ typedef struct {
   int32_t heads_per_wg;          /* heads per workgroup: 16 or 64, dividing H;
                                     0 = library default (64 if 64 divides H,
                                     else 16) */
-  int32_t min_tile_blocks;       /* smallest device tile in 32-token blocks (4) */
+  int32_t min_tile_blocks;       /* smallest device tile in cache blocks (4) */
   int32_t wgs_per_cu;            /* device tiling target: workgroups per CU (1) */
   int32_t force_partitions;      /* >0: every request gets P_b = this */
   int32_t force_splits;          /* >0: every request gets S_b = this */
@@ -139,7 +143,8 @@ void mla_default_plan_params(mla_plan_params* p);
  *
  * batch >= 0; num_heads in [16, 128], a multiple of 16; 1 <= q_len <=
  * MLA_MAX_QLEN;
- * context_lens_host[b] >= 0; block_size == 32. params may be NULL
+ * context_lens_host[b] >= 0; block_size 16 or 32 (nblk_b = ceil(n_b /
+ * block_size); tiles count blocks of that size). params may be NULL
  * (defaults). partitions_host, splits_host [batch] and row_indptr_host
  * [batch+1] are written; info may be NULL.
  * Errors: MLA_E_NULL, MLA_E_SHAPE, MLA_E_RANGE, MLA_E_UNSUPPORTED,
@@ -155,14 +160,16 @@ int mla_choose_partitions(int32_t batch, int32_t num_heads, int32_t q_len,
 /*
  * mla_partition_range -- the index math, exported for tests (host only).
  * Tokens [*tok_begin, *tok_end) of tile s of partition p of a context of
- * `ctx` tokens split into P partitions of S tiles each:
- *   nblk = ceil(ctx/32); bpp = ceil(nblk/P);
+ * `ctx` tokens in blocks of block_size (16 or 32) tokens, split into P
+ * partitions of S tiles each (BS = block_size):
+ *   nblk = ceil(ctx/BS); bpp = ceil(nblk/P);
  *   partition p = blocks [min(p*bpp, nblk), min((p+1)*bpp, nblk));
  *   with m blocks in it and bps = ceil(m/S), tile s = blocks
  *   [lo, hi) = [b0 + min(s*bps, m), b0 + min((s+1)*bps, m));
- *   tokens [min(lo*32, ctx), min(hi*32, ctx)).
+ *   tokens [min(lo*BS, ctx), min(hi*BS, ctx)).
  * The partition kernel computes exactly the same ranges on the device.
- * Errors: MLA_E_NULL, MLA_E_RANGE (ctx < 0, P/S/p/s out of range).
+ * Errors: MLA_E_NULL, MLA_E_RANGE (ctx < 0, P/S/p/s out of range),
+ * MLA_E_UNSUPPORTED (block_size not 16 or 32).
  */
 int mla_partition_range(int32_t ctx, int32_t block_size, int32_t P, int32_t S,
                         int32_t p, int32_t s, int32_t* tok_begin, int32_t* tok_end);
@@ -195,13 +202,16 @@ int mla_partition_range(int32_t ctx, int32_t block_size, int32_t P, int32_t S,
  * q_len       new tokens per request, 1 .. MLA_MAX_QLEN (the chooser's q_len)
  * q_absorbed  dev [batch, q_len, num_heads, 512]  16-bit, 16-byte aligned
  * q_pe        dev [batch, q_len, num_heads, 64]   16-bit, 16-byte aligned
- * ckv_cache   dev [num_blocks, 32, 512]       16-bit, 16-byte aligned
- * kpe_cache   dev [num_blocks, 32, 64]        16-bit, 16-byte aligned
+ * ckv_cache   dev [num_blocks, block_size, 512]  16-bit, 16-byte aligned
+ * kpe_cache   dev [num_blocks, block_size, 64]   16-bit, 16-byte aligned
+ * block_size  tokens per cache block: 32, or 16; it must be the block size
+ *             the plan was chosen for
  * block_table dev int32 [batch, max_blocks_per_seq]; entries below
- *             ceil(n_b/32) must lie in [0, num_blocks) (others are never
- *             read). An entry outside that range is clamped into it, never
- *             dereferenced out of bounds; the result is then unspecified.
- * context_lens dev int32 [batch], 0 <= n_b <= 32 * max_blocks_per_seq
+ *             ceil(n_b/block_size) must lie in [0, num_blocks) (others are
+ *             never read). An entry outside that range is clamped into it,
+ *             never dereferenced out of bounds; the result is then
+ *             unspecified.
+ * context_lens dev int32 [batch], 0 <= n_b <= block_size * max_blocks_per_seq
  *             (clamped into that range on the device). Rows of the last
  *             block at t >= n_b may hold anything, NaN included.
  * scale       softmax scale applied to both score halves (finite, > 0)
@@ -219,7 +229,7 @@ int mla_partition_range(int32_t ctx, int32_t block_size, int32_t P, int32_t S,
  * MLA_E_UNSUPPORTED, MLA_E_HIP.
  */
 int mla_decode_partition(const void* q_absorbed, const void* q_pe, const void* ckv_cache,
-                         const void* kpe_cache, int32_t num_blocks,
+                         const void* kpe_cache, int32_t num_blocks, int32_t block_size,
                          const int32_t* block_table, int32_t max_blocks_per_seq,
                          const int32_t* context_lens, int32_t batch, int32_t num_heads,
                          int32_t q_len, float scale, int32_t dtype, const int32_t* partitions,
@@ -285,7 +295,8 @@ int mla_decode_reduce(const float* partial_out, const float* partial_lse2,
  * Errors: as mla_decode_partition.
  */
 int mla_decode_fused(const void* q_absorbed, const void* q_pe, const void* ckv_cache,
-                     const void* kpe_cache, int32_t num_blocks, const int32_t* block_table,
+                     const void* kpe_cache, int32_t num_blocks, int32_t block_size,
+                     const int32_t* block_table,
                      int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch,
                      int32_t num_heads, int32_t q_len, float scale, int32_t dtype,
                      const int32_t* partitions,

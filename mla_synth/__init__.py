@@ -104,6 +104,7 @@ class Case:
     seed: int
     poisoned: bool = False
     q_len: int = 1             # new tokens per request; q rows are [B, q_len * H]
+    block_size: int = BLOCK_SIZE   # tokens per cache block (32, or 16)
 
     @property
     def num_blocks(self) -> int:
@@ -117,29 +118,29 @@ class Case:
         return int(self.context_lens.astype(np.int64).sum()) * (KV_LORA_RANK + ROPE_DIM) * 2
 
 
-def blocks_for(n: int) -> int:
-    return (int(n) + BLOCK_SIZE - 1) // BLOCK_SIZE
+def blocks_for(n: int, block_size: int = BLOCK_SIZE) -> int:
+    return (int(n) + block_size - 1) // block_size
 
 
 def make_case(seed: int, batch: int, heads: int, contexts=None, context_range=None,
               dtype: str = "f16", value_scale: float = 1.0, pool_factor: int = 2,
               pool_blocks: int | None = None, poison: bool = False,
               scale: float = DEFAULT_SCALE, max_blocks: int | None = None,
-              q_len: int = 1) -> Case:
+              q_len: int = 1, block_size: int = BLOCK_SIZE) -> Case:
     rng = np.random.Generator(np.random.PCG64(seed))
     if context_range is not None:
         lo, hi = context_range
         ctx = rng.integers(lo, hi, size=batch, endpoint=True).astype(np.int32)
     else:
         ctx = np.asarray(contexts, dtype=np.int32).reshape(batch)
-    nblk = [blocks_for(n) for n in ctx]
+    nblk = [blocks_for(n, block_size) for n in ctx]
     needed = int(sum(nblk))
     pool = int(pool_blocks) if pool_blocks is not None else max(1, pool_factor * needed)
     if pool < needed:
         raise ValueError("pool smaller than the blocks the batch needs")
     perm = rng.permutation(pool).astype(np.int32)
-    ckv = _draw16(rng, (pool, BLOCK_SIZE, KV_LORA_RANK), dtype, value_scale)
-    kpe = _draw16(rng, (pool, BLOCK_SIZE, ROPE_DIM), dtype, value_scale)
+    ckv = _draw16(rng, (pool, block_size, KV_LORA_RANK), dtype, value_scale)
+    kpe = _draw16(rng, (pool, block_size, ROPE_DIM), dtype, value_scale)
     qa = _draw16(rng, (batch, q_len * heads, KV_LORA_RANK), dtype, value_scale)
     qp = _draw16(rng, (batch, q_len * heads, ROPE_DIM), dtype, value_scale)
 
@@ -160,7 +161,8 @@ def make_case(seed: int, batch: int, heads: int, contexts=None, context_range=No
 
     case = Case(dtype=dtype, batch=batch, heads=heads, context_lens=ctx,
                 block_table=table, ckv_pool=ckv, kpe_pool=kpe, q_absorbed=qa,
-                q_pe=qp, scale=float(scale), seed=seed, q_len=int(q_len))
+                q_pe=qp, scale=float(scale), seed=seed, q_len=int(q_len),
+                block_size=int(block_size))
     if poison:
         poison_case(case)
     return case
@@ -171,16 +173,17 @@ def poison_case(case: Case) -> None:
     nan = np.uint16(NAN_BITS[case.dtype])
     used = np.zeros(case.num_blocks, dtype=bool)
     for b in range(case.batch):
-        k = blocks_for(case.context_lens[b])
+        k = blocks_for(case.context_lens[b], case.block_size)
         used[case.block_table[b, :k]] = True
     case.ckv_pool[~used] = nan
     case.kpe_pool[~used] = nan
     for b in range(case.batch):
         n = int(case.context_lens[b])
-        if n % BLOCK_SIZE:
-            last = case.block_table[b, blocks_for(n) - 1]
-            case.ckv_pool[last, n % BLOCK_SIZE:] = nan
-            case.kpe_pool[last, n % BLOCK_SIZE:] = nan
+        bs = case.block_size
+        if n % bs:
+            last = case.block_table[b, blocks_for(n, bs) - 1]
+            case.ckv_pool[last, n % bs:] = nan
+            case.kpe_pool[last, n % bs:] = nan
     case.poisoned = True
 
 
@@ -216,6 +219,11 @@ WORKLOADS = {
 
 
 def make_workload(name: str, **overrides) -> Case:
+    """A named workload; block_size=16 stores the same contexts in 16-token
+    blocks (a fixed pool size is doubled to hold the same tokens)."""
     spec = dict(WORKLOADS[name])
+    bs = int(overrides.get("block_size", BLOCK_SIZE))
+    if "pool_blocks" in spec and bs != BLOCK_SIZE:
+        spec["pool_blocks"] = spec["pool_blocks"] * BLOCK_SIZE // bs
     spec.update(overrides)
     return make_case(**spec)

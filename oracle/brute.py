@@ -38,15 +38,16 @@ def _row(pool, phys, slot, dtype):
 def latent_brute(case, b: int, h: int):
     """out[b, h] (list of 512 mpf) and lse2[b, h] (mpf) by the definition."""
     n = int(case.context_lens[b])
+    bs = int(case.ckv_pool.shape[1])   # tokens per cache block
     qa = [_bits_to_mpf(v, case.dtype) for v in case.q_absorbed[b][h]]
     qp = [_bits_to_mpf(v, case.dtype) for v in case.q_pe[b][h]]
     scale = mpmath.mpf(case.scale)
     num = [mpmath.mpf(0)] * len(qa)
     den = mpmath.mpf(0)
     for t in range(n):
-        phys = int(case.block_table[b][t // 32])
-        c = _row(case.ckv_pool, phys, t % 32, case.dtype)
-        k = _row(case.kpe_pool, phys, t % 32, case.dtype)
+        phys = int(case.block_table[b][t // bs])
+        c = _row(case.ckv_pool, phys, t % bs, case.dtype)
+        k = _row(case.kpe_pool, phys, t % bs, case.dtype)
         s = scale * (mpmath.fsum(x * y for x, y in zip(qa, c))
                      + mpmath.fsum(x * y for x, y in zip(qp, k)))
         e = mpmath.exp(s)
@@ -63,6 +64,7 @@ def latent_brute_window(case, b: int, j: int, h: int):
     definition with an explicit causal mask: token j sits at position
     pos = n - q_len + j and every t > pos is skipped."""
     n = int(case.context_lens[b])
+    bs = int(case.ckv_pool.shape[1])   # tokens per cache block
     pos = n - int(case.q_len) + j
     row = j * case.heads + h
     qa = [_bits_to_mpf(v, case.dtype) for v in case.q_absorbed[b][row]]
@@ -73,9 +75,9 @@ def latent_brute_window(case, b: int, j: int, h: int):
     for t in range(n):
         if t > pos:
             continue
-        phys = int(case.block_table[b][t // 32])
-        c = _row(case.ckv_pool, phys, t % 32, case.dtype)
-        k = _row(case.kpe_pool, phys, t % 32, case.dtype)
+        phys = int(case.block_table[b][t // bs])
+        c = _row(case.ckv_pool, phys, t % bs, case.dtype)
+        k = _row(case.kpe_pool, phys, t % bs, case.dtype)
         s = scale * (mpmath.fsum(x * y for x, y in zip(qa, c))
                      + mpmath.fsum(x * y for x, y in zip(qp, k)))
         e = mpmath.exp(s)
@@ -93,6 +95,7 @@ def decompressed_brute(case, b: int, h: int, q_nope, W_UK, W_UV_T):
     q_nope [dn] floats; W_UK [dn, 512]; W_UV_T [512, dv] (plain floats).
     """
     n = int(case.context_lens[b])
+    bs = int(case.ckv_pool.shape[1])   # tokens per cache block
     qn = [mpmath.mpf(float(x)) for x in q_nope]
     qp = [_bits_to_mpf(v, case.dtype) for v in case.q_pe[b][h]]
     scale = mpmath.mpf(case.scale)
@@ -101,9 +104,9 @@ def decompressed_brute(case, b: int, h: int, q_nope, W_UK, W_UV_T):
     num = [mpmath.mpf(0)] * dv
     den = mpmath.mpf(0)
     for t in range(n):
-        phys = int(case.block_table[b][t // 32])
-        c = _row(case.ckv_pool, phys, t % 32, case.dtype)
-        k = _row(case.kpe_pool, phys, t % 32, case.dtype)
+        phys = int(case.block_table[b][t // bs])
+        c = _row(case.ckv_pool, phys, t % bs, case.dtype)
+        k = _row(case.kpe_pool, phys, t % bs, case.dtype)
         key = [mpmath.fsum(mpmath.mpf(float(W_UK[d][i])) * c[i] for i in range(len(c)))
                for d in range(dn)]
         val = [mpmath.fsum(c[i] * mpmath.mpf(float(W_UV_T[i][j])) for i in range(len(c)))

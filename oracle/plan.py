@@ -35,17 +35,21 @@ Workspace shedding, when a limit is set and exceeded, in order:
      until the limit holds;
   still over the limit -> error (possible only with forced values).
 
-Index math. With nblk = ceil(n/32):
+Index math. With cache blocks of BS tokens (32, the pages' block size, or
+16, the "block16" layout the vllm-metal pull request's review asks to see
+covered) and nblk = ceil(n/BS):
   partition p of P covers blocks [min(p*bpp, nblk), min((p+1)*bpp, nblk)),
   bpp = ceil(nblk / P); tile s of S inside a partition of m blocks covers
   [b0 + min(s*bps, m), b0 + min((s+1)*bps, m)), bps = ceil(m / S); its
-  tokens are [min(lo*32, n), min(hi*32, n)).
+  tokens are [min(lo*BS, n), min(hi*BS, n)). The chooser's nblk_b and tile
+  count blocks of the same size.
 """
 from __future__ import annotations
 
 import dataclasses
 
 BLOCK_SIZE = 32
+BLOCK_SIZES = (16, 32)
 LATENT = 512
 MAX_PARTITIONS = 8
 MAX_SPLITS = 4096
@@ -110,7 +114,7 @@ def choose_partitions(batch: int, heads: int, q_len: int, ctx, params: PlanParam
                       block_size: int = BLOCK_SIZE):
     """Mirror of mla_choose_partitions. Raises ValueError on invalid input."""
     prm = params or PlanParams()
-    if batch < 0 or q_len < 1 or q_len > MAX_QLEN or block_size != BLOCK_SIZE:
+    if batch < 0 or q_len < 1 or q_len > MAX_QLEN or block_size not in BLOCK_SIZES:
         raise ValueError("shape")
     if heads < 16 or heads > 128 or heads % 16:
         raise ValueError("unsupported heads")

@@ -11,7 +11,6 @@ import math
 
 import numpy as np
 
-BLOCK_SIZE = 32
 LATENT = 512
 ROPE = 64
 # log2(e); the split path's LSE is in base 2 (mlxcel pull request 995, "How
@@ -34,18 +33,20 @@ def gather_request(ckv_pool, kpe_pool, table_row, n: int, dtype: str,
                    lo: int = 0, hi: int | None = None):
     """Tokens [lo, hi) of one request, read through its block table.
 
-    Token t lives in physical block table_row[t // 32], slot t % 32
-    (vllm-metal pull request 601, "Wrapper benchmark": block size 32 paged
-    cache with a block table). Only t < n is ever read.
+    Token t lives in physical block table_row[t // BS], slot t % BS, where
+    BS = ckv_pool.shape[1] is the block size (vllm-metal pull request 601,
+    "Wrapper benchmark": block size 32 paged cache with a block table; its
+    review also asks for blocks of 16). Only t < n is ever read.
     Returns (C [k, 512], Kp [k, 64]) in float64.
     """
     hi = n if hi is None else min(hi, n)
     lo = max(0, lo)
     if hi <= lo:
         return np.zeros((0, LATENT)), np.zeros((0, ROPE))
+    bs = int(ckv_pool.shape[1])
     t = np.arange(lo, hi)
-    phys = np.asarray(table_row)[t // BLOCK_SIZE]
-    slot = t % BLOCK_SIZE
+    phys = np.asarray(table_row)[t // bs]
+    slot = t % bs
     C = decode16(ckv_pool[phys, slot], dtype)
     Kp = decode16(kpe_pool[phys, slot], dtype)
     return C, Kp

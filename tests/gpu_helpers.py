@@ -47,7 +47,8 @@ def run_case(case, params: mla.PlanParams | None = None, dev=None, want_ranges=F
     import torch
     dev = dev or to_device(case)
     q_len = int(getattr(case, "q_len", 1))
-    plan = mla.DecodePlan(case.context_lens, case.heads, params, q_len=q_len)
+    plan = mla.DecodePlan(case.context_lens, case.heads, params, q_len=q_len,
+                          block_size=int(getattr(case, "block_size", 32)))
     rows = q_len * case.heads
     out = torch.empty((case.batch, rows, 512), dtype=torch_dtype(case.dtype), device="cuda")
     lse2 = torch.empty((case.batch, rows), dtype=torch.float32, device="cuda")
@@ -101,7 +102,8 @@ def check_sync_quiet(plan, what=""):
 
 
 def rows_of_plan(case, plan):
-    return oracle.row_ranges(case.context_lens, plan.info["P"], plan.info["S"])
+    return oracle.row_ranges(case.context_lens, plan.info["P"], plan.info["S"],
+                             block_size=int(getattr(case, "block_size", 32)))
 
 
 def device_cus() -> int:

@@ -56,15 +56,16 @@ def test_default_params_match_header_and_mirror():
     assert d.num_cus == 0 and d.heads_per_wg == 0
 
 
-def _both(batch, heads, q_len, ctx, **kw):
+def _both(batch, heads, q_len, ctx, block_size=32, **kw):
     c_params = mla.PlanParams(**kw)
     m_params = mirror.PlanParams(**kw)
     try:
-        ref = mirror.choose_partitions(batch, heads, q_len, ctx, m_params)
+        ref = mirror.choose_partitions(batch, heads, q_len, ctx, m_params, block_size=block_size)
     except ValueError:
         ref = None
     try:
-        got = mla.mla_choose_partitions(batch, heads, q_len, ctx, c_params)
+        got = mla.mla_choose_partitions(batch, heads, q_len, ctx, c_params,
+                                        block_size=block_size)
     except mla.MlaError:
         got = None
     return ref, got
@@ -80,9 +81,10 @@ def _same(ref, got):
     assert ref["workspace_bytes"] == got["partial_out_bytes"] + got["partial_lse_bytes"]
 
 
+@pytest.mark.parametrize("block_size", [32, 16])
 @pytest.mark.parametrize("heads", [16, 32, 64, 128])
-def test_chooser_matches_mirror_on_a_grid(heads):
-    rng = np.random.default_rng(heads)
+def test_chooser_matches_mirror_on_a_grid(heads, block_size):
+    rng = np.random.default_rng(heads + block_size)
     ctx_pool = [0, 1, 31, 32, 33, 1000, 4096, 20000, 32767, 32768, 49152, 65536, 81920,
                 98304, 131072]
     for batch in (1, 2, 3, 8):
@@ -90,7 +92,8 @@ def test_chooser_matches_mirror_on_a_grid(heads):
             ctx = [int(c) for c in rng.choice(ctx_pool, size=batch)]
             for num_cus, tile, limit, fp, fs, hpw in itertools.product(
                     (8, 256), (1, 4), (0, 1 << 20, 64 << 20), (0, 3), (0, 2), (0, 16, heads)):
-                ref, got = _both(batch, heads, 1, ctx, num_cus=num_cus, min_tile_blocks=tile,
+                ref, got = _both(batch, heads, 1, ctx, block_size, num_cus=num_cus,
+                                 min_tile_blocks=tile,
                                  workspace_limit_bytes=limit, force_partitions=fp,
                                  force_splits=fs, heads_per_wg=hpw)
                 _same(ref, got)
@@ -105,8 +108,8 @@ def test_chooser_matches_mirror_on_workloads():
             ctx = [int(c) for c in rng.integers(lo, hi, size=spec["batch"], endpoint=True)]
         else:
             ctx = spec["contexts"]
-        for limit in (0, 64 << 20):
-            ref, got = _both(spec["batch"], spec["heads"], 1, ctx, num_cus=256,
+        for limit, bs in itertools.product((0, 64 << 20), (32, 16)):
+            ref, got = _both(spec["batch"], spec["heads"], 1, ctx, bs, num_cus=256,
                              workspace_limit_bytes=limit)
             _same(ref, got)
             assert got is not None
@@ -126,16 +129,20 @@ def test_chooser_pure_decode_and_errors():
     for q in (2, 4, 8):
         _same(*_both(3, 32, q, [40000, 7, 3000], num_cus=256))
         _same(*_both(1, 128, q, [131072], num_cus=256))
-    with pytest.raises(mla.MlaError) as e:
-        mla.mla_choose_partitions(1, 16, 1, [10], mla.PlanParams(num_cus=256), block_size=16)
-    assert e.value.status == -6
+    for bs in (8, 24, 64):
+        with pytest.raises(mla.MlaError) as e:
+            mla.mla_choose_partitions(1, 16, 1, [10], mla.PlanParams(num_cus=256), block_size=bs)
+        assert e.value.status == -6
+        ref, got = _both(1, 16, 1, [10], bs, num_cus=256)
+        assert ref is None and got is None
     with pytest.raises(mla.MlaError) as e:
         mla.mla_choose_partitions(1, 16, 1, [4096], mla.PlanParams(
             num_cus=256, force_partitions=4, force_splits=4, workspace_limit_bytes=1000))
     assert e.value.status == -5 and "workspace" in mla.mla_last_error()
 
 
-def test_index_math_matches_mirror_exhaustively_small():
+@pytest.mark.parametrize("block_size", [32, 16])
+def test_index_math_matches_mirror_exhaustively_small(block_size):
     # Every context up to 300 tokens, every P <= 8, S <= 16, every (p, s).
     lib = mla.load_library()
     lo, hi = ctypes.c_int32(), ctypes.c_int32()
@@ -144,9 +151,10 @@ def test_index_math_matches_mirror_exhaustively_small():
             for S in range(1, 17):
                 for p in range(P):
                     for s in range(S):
-                        assert lib.mla_partition_range(n, 32, P, S, p, s, ctypes.byref(lo),
-                                                       ctypes.byref(hi)) == 0
-                        assert (lo.value, hi.value) == mirror.partition_range(n, P, S, p, s)
+                        assert lib.mla_partition_range(n, block_size, P, S, p, s,
+                                                       ctypes.byref(lo), ctypes.byref(hi)) == 0
+                        assert (lo.value, hi.value) == \
+                            mirror.partition_range(n, P, S, p, s, block_size)
 
 
 def test_index_math_matches_mirror_at_long_contexts():
@@ -159,8 +167,9 @@ def test_index_math_matches_mirror_at_long_contexts():
                 for p in range(P):
                     for s in sorted({0, 1, S // 2, S - 1}):
                         if s < S:
-                            assert mla.mla_partition_range(n, P, S, p, s) == \
-                                mirror.partition_range(n, P, S, p, s)
+                            for bs in (32, 16):
+                                assert mla.mla_partition_range(n, P, S, p, s, bs) == \
+                                    mirror.partition_range(n, P, S, p, s, bs)
 
 
 def test_index_math_errors():
@@ -178,11 +187,12 @@ def test_decode_partition_host_checks_launch_nothing():
     odd = vp(0x10008)
 
     def call(**kw):
-        a = dict(qa=good, qp=good, ckv=good, kpe=good, nblk=4, tbl=good, maxb=4, ctx=good,
+        a = dict(qa=good, qp=good, ckv=good, kpe=good, nblk=4, bs=32, tbl=good, maxb=4, ctx=good,
                  batch=1, heads=16, qlen=1, scale=0.07, dtype=0, P=good, S=good, ind=good, rows=2,
                  maxr=2, hpw=0, po=good, pl=good, out=good, lo=None, dbg=None, stream=None)
         a.update(kw)
-        return lib.mla_decode_partition(a["qa"], a["qp"], a["ckv"], a["kpe"], a["nblk"], a["tbl"],
+        return lib.mla_decode_partition(a["qa"], a["qp"], a["ckv"], a["kpe"], a["nblk"], a["bs"],
+                                        a["tbl"],
                                         a["maxb"], a["ctx"], a["batch"], a["heads"], a["qlen"],
                                         a["scale"],
                                         a["dtype"], a["P"], a["S"], a["ind"], a["rows"], a["maxr"],
@@ -193,6 +203,8 @@ def test_decode_partition_host_checks_launch_nothing():
     assert call(qlen=0) == -6
     assert call(qlen=9) == -6
     assert call(dtype=7) == -6
+    assert call(bs=64) == -6             # cache blocks of 16 or 32 tokens only
+    assert call(bs=8) == -6
     assert call(hpw=32) == -6
     assert call(heads=128, hpw=128) == -6   # no 128-head layout
     assert call(heads=96, hpw=64) == -6     # 64 must divide H
@@ -216,12 +228,13 @@ def test_decode_fused_host_checks_launch_nothing():
     good = vp(0x10000)
 
     def call(**kw):
-        a = dict(qa=good, qp=good, ckv=good, kpe=good, nblk=4, tbl=good, maxb=4, ctx=good,
+        a = dict(qa=good, qp=good, ckv=good, kpe=good, nblk=4, bs=32, tbl=good, maxb=4, ctx=good,
                  batch=1, heads=16, qlen=1, scale=0.07, dtype=0, P=good, S=good, ind=good, rows=2,
                  maxr=2, hpw=0, po=good, pl=good, out=good, lo=None, sync=good, dbg=None,
                  stream=None)
         a.update(kw)
-        return lib.mla_decode_fused(a["qa"], a["qp"], a["ckv"], a["kpe"], a["nblk"], a["tbl"],
+        return lib.mla_decode_fused(a["qa"], a["qp"], a["ckv"], a["kpe"], a["nblk"], a["bs"],
+                                    a["tbl"],
                                     a["maxb"], a["ctx"], a["batch"], a["heads"], a["qlen"],
                                     a["scale"],
                                     a["dtype"], a["P"], a["S"], a["ind"], a["rows"], a["maxr"],
@@ -232,6 +245,7 @@ def test_decode_fused_host_checks_launch_nothing():
     assert call(sync=vp(0x10020)) == -4      # sync must be 64-byte aligned
     assert call(heads=128, hpw=16, qlen=2) == -6   # 16 head groups: more than the record holds
     assert call(heads=24) == -6
+    assert call(bs=48) == -6
     assert call(po=None) == -1
     assert call(batch=0) == 0
 

@@ -447,3 +447,81 @@ def test_window_needle_visibility():
                 assert np.max(np.abs(after[0, row] - needle)) < 1e-12
             else:
                 assert np.array_equal(before[0, row], after[0, row])
+
+
+# --- Blocks of 16 tokens (the "block16" layout vllm-metal pull request 601's
+# review asks to see covered) ------------------------------------------------
+
+def relayout_16(case):
+    """The same logical tokens stored as 16-token blocks: block k of 32
+    tokens becomes blocks 2k and 2k + 1 of the new pool, in a fresh random
+    order, and the table is rewritten to match."""
+    pool32 = case.num_blocks
+    ckv = case.ckv_pool.reshape(pool32 * 2, 16, 512)
+    kpe = case.kpe_pool.reshape(pool32 * 2, 16, 64)
+    perm = np.random.default_rng(7).permutation(pool32 * 2)   # new slot of old half i
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(perm.size)
+    table = np.empty((case.batch, case.max_blocks * 2), dtype=np.int32)
+    table[:, 0::2] = perm[2 * case.block_table]
+    table[:, 1::2] = perm[2 * case.block_table + 1]
+    return mla_synth.Case(dtype=case.dtype, batch=case.batch, heads=case.heads,
+                          context_lens=case.context_lens.copy(), block_table=table,
+                          ckv_pool=ckv[inv].copy(), kpe_pool=kpe[inv].copy(),
+                          q_absorbed=case.q_absorbed, q_pe=case.q_pe, scale=case.scale,
+                          seed=case.seed, q_len=case.q_len, block_size=16)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("contexts", [[1], [15, 16], [17, 33], [70]])
+def test_block16_latent_matches_brute_force(dtype, contexts):
+    # Generated directly with 16-token blocks; the brute force walks the
+    # table itself, slot t % 16 of block t // 16.
+    case = small_case(401 + len(contexts) + contexts[0], contexts, dtype=dtype, poison=True,
+                      block_size=16)
+    assert case.ckv_pool.shape[1] == 16
+    out, lse2 = oracle.latent_f64(case)
+    for b in range(case.batch):
+        for h in range(case.heads):
+            eo, el = _brute_errors(case, b, h, out, lse2)
+            assert eo < 1e-12 and el < 1e-12, (b, h, eo, el)
+
+
+@pytest.mark.parametrize("contexts", [[200, 17], [1024], [16, 31, 32, 33]])
+def test_block16_relayout_is_bit_identical(contexts):
+    # The answer depends on the logical token sequence only, not on how the
+    # cache cuts it into blocks.
+    case = small_case(411 + len(contexts), contexts, heads=3, dtype="bf16")
+    out, lse2 = oracle.latent_f64(case)
+    c16 = relayout_16(case)
+    out16, lse16 = oracle.latent_f64(c16)
+    assert np.array_equal(out, out16) and np.array_equal(lse2, lse16)
+
+
+@pytest.mark.parametrize("contexts", [[1000], [33, 97, 1, 16]])
+def test_block16_split_merge_equals_single_pass(contexts):
+    case = small_case(421 + len(contexts), contexts, heads=2, block_size=16)
+    ref, lref = oracle.latent_f64(case)
+    for P in (1, 2, 5, 8):
+        for S in (1, 3, 7):
+            Ps, Ss = [P] * case.batch, [S] * case.batch
+            ranges = oracle.row_ranges(case.context_lens, Ps, Ss, block_size=16)
+            assert all(lo % 16 == 0 for _, lo, hi in ranges if hi > lo)
+            indptr = np.concatenate([[0], np.cumsum([p * s for p, s in zip(Ps, Ss)])])
+            po, pl = oracle.partials_f64(case, ranges, indptr)
+            out, lse2 = oracle.merge_log2_f64(po, pl, indptr)
+            assert np.max(np.abs(out - ref)) < 1e-13, (P, S)
+            assert np.max(np.abs(lse2 - lref)) < 1e-12, (P, S)
+
+
+@pytest.mark.parametrize("t", [0, 15, 16, 31, 47, 199])
+def test_block16_needle_is_found(t):
+    case = small_case(431, [200], heads=2, block_size=16)
+    phys = case.block_table[0, t // 16]
+    sign = np.sign(reference.decode16(case.q_absorbed[0, 1], case.dtype))
+    sign[sign == 0] = 1
+    case.ckv_pool[phys, t % 16] = mla_synth.encode16((6.0 * sign).astype(np.float32), case.dtype)
+    case.kpe_pool[phys, t % 16] = mla_synth.encode16(np.zeros(64, np.float32), case.dtype)
+    needle = reference.decode16(case.ckv_pool[phys, t % 16], case.dtype)
+    out, _ = oracle.latent_f64(case)
+    assert np.max(np.abs(out[0, 1] - needle)) < 1e-12
