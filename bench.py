@@ -46,9 +46,11 @@ FETCH_SCALE = 2.0
 WRITE_SCALE = 1.0
 MEASURED = {
     # profiles/partition_kernel_v2lite_32k.md
-    ("v2lite_32k", "35cfabb12306"): dict(fetch_kib=18630.0, write_kib=8208.0, mfma_busy=0.020),
+    ("v2lite_32k", "6979dc04a8bc"): dict(fetch_kib=18631.0, write_kib=8208.0, mfma_busy=0.020),
+    ("v2lite_32k@bs16", "6979dc04a8bc"): dict(fetch_kib=18638.0, write_kib=8208.0,
+                                              mfma_busy=0.021),
     # profiles/wide_kernel_v3_131k.md
-    ("v3_131k", "1cba2bacb378"): dict(fetch_kib=74491.7, write_kib=32832.0, mfma_busy=0.285),
+    ("v3_131k", "cf00c39304d6"): dict(fetch_kib=74503.0, write_kib=32832.0, mfma_busy=0.282),
 }
 
 
