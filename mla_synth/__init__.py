@@ -29,6 +29,13 @@ point at a block no request uses.
 With ``poison=True`` every unreferenced pool block and every row past the
 context end in a request's last block is filled with NaN: a correct kernel
 never lets those rows reach its output.
+
+With ``kv_dtype="fp8_e4m3"`` the two cache pools are stored one byte per
+value in the E4M3 format of the OCP 8-bit floating point specification
+(exponent bias 7, 3 mantissa bits, max 448, NaN = S.1111.111, no
+infinities): each drawn value v (times value_scale) is stored as the code
+nearest to v / kv_scale, ties to the even code, saturating at 448. Queries
+stay 16-bit. The pages keep 16-bit caches only; this layout is ours.
 """
 from __future__ import annotations
 
@@ -44,6 +51,36 @@ ROPE_DIM = 64
 DEFAULT_SCALE = 1.0 / math.sqrt(192.0)
 
 NAN_BITS = {"f16": 0x7E00, "bf16": 0x7FC0}
+FP8_NAN = 0x7F          # E4M3 NaN (S.1111.111)
+FP8_MAX = 448.0         # largest finite E4M3 value
+
+
+def _fp8_positive_table() -> np.ndarray:
+    """Values of the E4M3 codes 0x00..0x7E (OCP 8-bit floating point, E4M3:
+    exponent bias 7, three mantissa bits, subnormals at exponent field 0, no
+    infinities), ascending. Used only to encode inputs."""
+    vals = []
+    for code in range(0x7F):
+        e, m = code >> 3, code & 7
+        vals.append(m / 8.0 * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return np.asarray(vals, dtype=np.float64)
+
+
+_FP8_TABLE = _fp8_positive_table()
+
+
+def f32_to_fp8_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round values to E4M3 (nearest, ties to the even code), saturating at
+    +-448; return raw bytes. Inputs here are finite."""
+    y = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(y), FP8_MAX)
+    hi = np.clip(np.searchsorted(_FP8_TABLE, a, side="left"), 0, _FP8_TABLE.size - 1)
+    lo = np.maximum(hi - 1, 0)
+    dlo = a - _FP8_TABLE[lo]
+    dhi = _FP8_TABLE[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(y), code | np.uint8(0x80), code).astype(np.uint8)
 
 
 def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
@@ -88,6 +125,24 @@ def _draw16(rng: np.random.Generator, shape, dtype: str, value_scale: float,
     return out
 
 
+def _draw8(rng: np.random.Generator, shape, value_scale: float, kv_scale: float,
+           chunk_rows: int = 1 << 22) -> np.ndarray:
+    """Draw standard normals in float32 (times value_scale) and store each
+    value v as the E4M3 code nearest to v / kv_scale, a chunk at a time."""
+    shape = tuple(int(s) for s in shape)
+    out = np.empty(shape, dtype=np.uint8)
+    flat = out.reshape(-1)
+    pos = 0
+    while pos < flat.size:
+        k = min(max(1, chunk_rows), flat.size - pos)
+        v = rng.standard_normal(k, dtype=np.float32)
+        if value_scale != 1.0:
+            v *= np.float32(value_scale)
+        flat[pos:pos + k] = f32_to_fp8_e4m3_bits(v.astype(np.float64) / kv_scale)
+        pos += k
+    return out
+
+
 @dataclasses.dataclass
 class Case:
     """One decode batch: raw 16-bit payloads plus int32 metadata."""
@@ -105,6 +160,11 @@ class Case:
     poisoned: bool = False
     q_len: int = 1             # new tokens per request; q rows are [B, q_len * H]
     block_size: int = BLOCK_SIZE   # tokens per cache block (32, or 16)
+    # Latent cache storage: None = the 16-bit dtype above; "fp8_e4m3" = one
+    # E4M3 byte per value, the stored value times kv_scale (one scale for the
+    # ckv and kpe pools).
+    kv_dtype: str | None = None
+    kv_scale: float = 1.0
 
     @property
     def num_blocks(self) -> int:
@@ -126,7 +186,8 @@ def make_case(seed: int, batch: int, heads: int, contexts=None, context_range=No
               dtype: str = "f16", value_scale: float = 1.0, pool_factor: int = 2,
               pool_blocks: int | None = None, poison: bool = False,
               scale: float = DEFAULT_SCALE, max_blocks: int | None = None,
-              q_len: int = 1, block_size: int = BLOCK_SIZE) -> Case:
+              q_len: int = 1, block_size: int = BLOCK_SIZE, kv_dtype: str | None = None,
+              kv_scale: float = 1.0) -> Case:
     rng = np.random.Generator(np.random.PCG64(seed))
     if context_range is not None:
         lo, hi = context_range
@@ -139,8 +200,14 @@ def make_case(seed: int, batch: int, heads: int, contexts=None, context_range=No
     if pool < needed:
         raise ValueError("pool smaller than the blocks the batch needs")
     perm = rng.permutation(pool).astype(np.int32)
-    ckv = _draw16(rng, (pool, block_size, KV_LORA_RANK), dtype, value_scale)
-    kpe = _draw16(rng, (pool, block_size, ROPE_DIM), dtype, value_scale)
+    if kv_dtype is None:
+        ckv = _draw16(rng, (pool, block_size, KV_LORA_RANK), dtype, value_scale)
+        kpe = _draw16(rng, (pool, block_size, ROPE_DIM), dtype, value_scale)
+    elif kv_dtype == "fp8_e4m3":
+        ckv = _draw8(rng, (pool, block_size, KV_LORA_RANK), value_scale, kv_scale)
+        kpe = _draw8(rng, (pool, block_size, ROPE_DIM), value_scale, kv_scale)
+    else:
+        raise ValueError(f"unknown kv_dtype {kv_dtype!r}")
     qa = _draw16(rng, (batch, q_len * heads, KV_LORA_RANK), dtype, value_scale)
     qp = _draw16(rng, (batch, q_len * heads, ROPE_DIM), dtype, value_scale)
 
@@ -162,7 +229,7 @@ def make_case(seed: int, batch: int, heads: int, contexts=None, context_range=No
     case = Case(dtype=dtype, batch=batch, heads=heads, context_lens=ctx,
                 block_table=table, ckv_pool=ckv, kpe_pool=kpe, q_absorbed=qa,
                 q_pe=qp, scale=float(scale), seed=seed, q_len=int(q_len),
-                block_size=int(block_size))
+                block_size=int(block_size), kv_dtype=kv_dtype, kv_scale=float(kv_scale))
     if poison:
         poison_case(case)
     return case
@@ -170,7 +237,7 @@ def make_case(seed: int, batch: int, heads: int, contexts=None, context_range=No
 
 def poison_case(case: Case) -> None:
     """Fill unreferenced blocks and the rows past each context end with NaN."""
-    nan = np.uint16(NAN_BITS[case.dtype])
+    nan = np.uint8(FP8_NAN) if case.kv_dtype else np.uint16(NAN_BITS[case.dtype])
     used = np.zeros(case.num_blocks, dtype=bool)
     for b in range(case.batch):
         k = blocks_for(case.context_lens[b], case.block_size)

@@ -33,12 +33,16 @@ What it computes, and where each piece comes from:
   used to pin the f64 functions on tiny inputs.
 * ``byte_model`` -- KV bytes per token, latent vs decompressed (mlxcel pull
   request 995, commit "performance-validation report").
+* ``reference.decode_fp8_e4m3`` -- E4M3 bytes to values, from the E4M3
+  definition of the OCP 8-bit floating point specification, for latent
+  caches stored in 8 bits with one scale (the pages keep 16-bit caches and
+  decline others; this cache variant and its single scale are our reading).
 
 Every function here is pinned by a ``-m "not gpu"`` test against something
 other than itself (closed forms, brute force, invariances, the pages'
 printed byte counts). None is "parity unpinned".
 """
-from .reference import (LOG2_E, decode16, gather_request, latent_f64,
+from .reference import (LOG2_E, decode16, decode_fp8_e4m3, gather_request, latent_f64,
                         latent_one, decompressed_f64, absorb_query,
                         unabsorb_output, partials_f64, merge_log2_f64,
                         merge_ln_wrong, orthogonal_weights)
@@ -48,7 +52,7 @@ from .byte_model import (latent_bytes_per_token, decompressed_bytes_per_token,
                          max_context_tokens)
 
 __all__ = [
-    "LOG2_E", "decode16", "gather_request", "latent_f64", "latent_one",
+    "LOG2_E", "decode16", "decode_fp8_e4m3", "gather_request", "latent_f64", "latent_one",
     "decompressed_f64", "absorb_query", "unabsorb_output", "partials_f64",
     "merge_log2_f64", "merge_ln_wrong", "orthogonal_weights", "PlanParams",
     "choose_partitions", "partition_range", "row_ranges",

@@ -35,6 +35,29 @@ def _row(pool, phys, slot, dtype):
     return [_bits_to_mpf(v, dtype) for v in pool[phys][slot]]
 
 
+def _fp8_to_mpf(code: int):
+    """One E4M3 byte by the OCP 8-bit floating point definition, case by
+    case: exponent field 0 is subnormal (m * 2^-9), 15 with mantissa 7 is
+    NaN, otherwise (8 + m) * 2^(e - 10)."""
+    code = int(code)
+    neg = code >= 128
+    e, m = (code >> 3) & 15, code & 7
+    if e == 15 and m == 7:
+        raise ValueError("non-finite input")
+    v = mpmath.mpf(m) * mpmath.mpf(2) ** -9 if e == 0 else \
+        mpmath.mpf(8 + m) * mpmath.mpf(2) ** (e - 10)
+    return -v if neg else v
+
+
+def _cache_row(case, pool, phys: int, slot: int):
+    """A cache row as mpf values: 16-bit rows, or E4M3 bytes times the
+    cache scale."""
+    if getattr(case, "kv_dtype", None) == "fp8_e4m3":
+        sc = mpmath.mpf(float(case.kv_scale))
+        return [_fp8_to_mpf(v) * sc for v in pool[phys][slot]]
+    return _row(pool, phys, slot, case.dtype)
+
+
 def latent_brute(case, b: int, h: int):
     """out[b, h] (list of 512 mpf) and lse2[b, h] (mpf) by the definition."""
     n = int(case.context_lens[b])
@@ -46,8 +69,8 @@ def latent_brute(case, b: int, h: int):
     den = mpmath.mpf(0)
     for t in range(n):
         phys = int(case.block_table[b][t // bs])
-        c = _row(case.ckv_pool, phys, t % bs, case.dtype)
-        k = _row(case.kpe_pool, phys, t % bs, case.dtype)
+        c = _cache_row(case, case.ckv_pool, phys, t % bs)
+        k = _cache_row(case, case.kpe_pool, phys, t % bs)
         s = scale * (mpmath.fsum(x * y for x, y in zip(qa, c))
                      + mpmath.fsum(x * y for x, y in zip(qp, k)))
         e = mpmath.exp(s)
@@ -76,8 +99,8 @@ def latent_brute_window(case, b: int, j: int, h: int):
         if t > pos:
             continue
         phys = int(case.block_table[b][t // bs])
-        c = _row(case.ckv_pool, phys, t % bs, case.dtype)
-        k = _row(case.kpe_pool, phys, t % bs, case.dtype)
+        c = _cache_row(case, case.ckv_pool, phys, t % bs)
+        k = _cache_row(case, case.kpe_pool, phys, t % bs)
         s = scale * (mpmath.fsum(x * y for x, y in zip(qa, c))
                      + mpmath.fsum(x * y for x, y in zip(qp, k)))
         e = mpmath.exp(s)
@@ -105,8 +128,8 @@ def decompressed_brute(case, b: int, h: int, q_nope, W_UK, W_UV_T):
     den = mpmath.mpf(0)
     for t in range(n):
         phys = int(case.block_table[b][t // bs])
-        c = _row(case.ckv_pool, phys, t % bs, case.dtype)
-        k = _row(case.kpe_pool, phys, t % bs, case.dtype)
+        c = _cache_row(case, case.ckv_pool, phys, t % bs)
+        k = _cache_row(case, case.kpe_pool, phys, t % bs)
         key = [mpmath.fsum(mpmath.mpf(float(W_UK[d][i])) * c[i] for i in range(len(c)))
                for d in range(dn)]
         val = [mpmath.fsum(c[i] * mpmath.mpf(float(W_UV_T[i][j])) for i in range(len(c)))

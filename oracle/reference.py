@@ -29,8 +29,34 @@ def decode16(bits: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
+def decode_fp8_e4m3(bits: np.ndarray) -> np.ndarray:
+    """Raw E4M3 bytes -> float64 values (exact), by the E4M3 definition of
+    the OCP 8-bit floating point specification: sign bit, 4-bit exponent
+    with bias 7, 3-bit mantissa; exponent field 0 holds the subnormals
+    m/8 * 2^-6; S.1111.111 is NaN; there are no infinities (so 448 is the
+    largest value)."""
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b >> 7, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 0xF) & (b & 0x7 == 0x7), np.nan, mag)
+    return sign * mag
+
+
+def decode_cache(rows: np.ndarray, dtype: str, kv_dtype=None, kv_scale: float = 1.0):
+    """Cache rows -> float64: 16-bit rows of `dtype`, or E4M3 bytes times
+    kv_scale when kv_dtype is "fp8_e4m3" (one scale for the whole latent
+    cache; our reading, since the pages keep 16-bit caches only)."""
+    if kv_dtype is None:
+        return decode16(rows, dtype)
+    if kv_dtype == "fp8_e4m3":
+        return decode_fp8_e4m3(rows) * float(kv_scale)
+    raise ValueError(f"unknown kv_dtype {kv_dtype!r}")
+
+
 def gather_request(ckv_pool, kpe_pool, table_row, n: int, dtype: str,
-                   lo: int = 0, hi: int | None = None):
+                   lo: int = 0, hi: int | None = None, kv_dtype=None, kv_scale: float = 1.0):
     """Tokens [lo, hi) of one request, read through its block table.
 
     Token t lives in physical block table_row[t // BS], slot t % BS, where
@@ -47,8 +73,8 @@ def gather_request(ckv_pool, kpe_pool, table_row, n: int, dtype: str,
     t = np.arange(lo, hi)
     phys = np.asarray(table_row)[t // bs]
     slot = t % bs
-    C = decode16(ckv_pool[phys, slot], dtype)
-    Kp = decode16(kpe_pool[phys, slot], dtype)
+    C = decode_cache(ckv_pool[phys, slot], dtype, kv_dtype, kv_scale)
+    Kp = decode_cache(kpe_pool[phys, slot], dtype, kv_dtype, kv_scale)
     return C, Kp
 
 
@@ -99,7 +125,8 @@ def latent_one(case, b: int, heads=None, lo: int = 0, hi: int | None = None):
     for j in sorted(set((rows // case.heads).tolist())):
         sel = rows // case.heads == j
         C, Kp = gather_request(case.ckv_pool, case.kpe_pool, case.block_table[b], n,
-                               case.dtype, lo, min(hi, visible_len(n, q_len, j)))
+                               case.dtype, lo, min(hi, visible_len(n, q_len, j)),
+                               getattr(case, "kv_dtype", None), getattr(case, "kv_scale", 1.0))
         qa = decode16(case.q_absorbed[b, rows[sel]], case.dtype)
         qp = decode16(case.q_pe[b, rows[sel]], case.dtype)
         out[sel], lse2[sel] = _attend(qa, qp, C, Kp, case.scale)
@@ -148,7 +175,8 @@ def decompressed_f64(case, q_nope, W_UK, W_UV_T, requests=None):
     for b in reqs:
         n = int(case.context_lens[b])
         C, Kp = gather_request(case.ckv_pool, case.kpe_pool, case.block_table[b], n,
-                               case.dtype)
+                               case.dtype, 0, None, getattr(case, "kv_dtype", None),
+                               getattr(case, "kv_scale", 1.0))
         qp = decode16(case.q_pe[b], case.dtype)
         for h in range(H):
             if n == 0:

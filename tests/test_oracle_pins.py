@@ -338,7 +338,7 @@ def _mutant_attend_sign(qa, qp, C, Kp, scale):
     return ORIG_ATTEND(-qa, -qp, C, Kp, scale)
 
 
-def _mutant_gather_off_by_one(ckv_pool, kpe_pool, table_row, n, dtype, lo=0, hi=None):
+def _mutant_gather_off_by_one(ckv_pool, kpe_pool, table_row, n, dtype, lo=0, hi=None, *rest):
     hi = n if hi is None else min(hi, n)
     t = np.arange(max(0, lo), hi)
     phys = np.asarray(table_row)[(t + 1) // 32]
@@ -347,8 +347,8 @@ def _mutant_gather_off_by_one(ckv_pool, kpe_pool, table_row, n, dtype, lo=0, hi=
             reference.decode16(kpe_pool[phys, slot], dtype))
 
 
-def _mutant_gather_drop_last(ckv_pool, kpe_pool, table_row, n, dtype, lo=0, hi=None):
-    return ORIG_GATHER(ckv_pool, kpe_pool, table_row, max(0, n - 1), dtype, lo, hi)
+def _mutant_gather_drop_last(ckv_pool, kpe_pool, table_row, n, dtype, lo=0, hi=None, *rest):
+    return ORIG_GATHER(ckv_pool, kpe_pool, table_row, max(0, n - 1), dtype, lo, hi, *rest)
 
 
 ORIG_ATTEND = reference._attend
@@ -525,3 +525,95 @@ def test_block16_needle_is_found(t):
     needle = reference.decode16(case.ckv_pool[phys, t % 16], case.dtype)
     out, _ = oracle.latent_f64(case)
     assert np.max(np.abs(out[0, 1] - needle)) < 1e-12
+
+
+# --- latent caches stored as E4M3 bytes with one scale --------------------------
+# The pages keep 16-bit caches; the 8-bit layout is the next step beyond them.
+# The byte format is the E4M3 format of the OCP 8-bit floating point
+# specification (bias 7, 3 mantissa bits, no infinities, S.1111.111 = NaN).
+
+def fp8_case(seed, contexts, heads=2, dtype="f16", kv_scale=0.0625, **kw):
+    return small_case(seed, contexts, heads=heads, dtype=dtype, kv_dtype="fp8_e4m3",
+                      kv_scale=kv_scale, **kw)
+
+
+def test_fp8_decode_closed_forms():
+    # Values fixed by the format definition: zero and negative zero, the
+    # smallest subnormal 2^-9 and the largest 7 * 2^-9, the smallest normal
+    # 2^-6, one, the largest finite value 1.75 * 2^8 = 448, and the two NaNs.
+    codes = np.array([0x00, 0x80, 0x01, 0x07, 0x08, 0x38, 0xB8, 0x7E, 0xFE, 0x40, 0x3C])
+    want = [0.0, -0.0, 2.0 ** -9, 7 * 2.0 ** -9, 2.0 ** -6, 1.0, -1.0, 448.0, -448.0, 2.0, 1.5]
+    got = reference.decode_fp8_e4m3(codes)
+    assert list(got) == want
+    assert np.signbit(got[1])
+    assert np.all(np.isnan(reference.decode_fp8_e4m3(np.array([0x7F, 0xFF]))))
+    # Finite positive codes are strictly increasing; the negative half mirrors them.
+    pos = reference.decode_fp8_e4m3(np.arange(0x7F))
+    assert np.all(np.diff(pos) > 0)
+    assert np.array_equal(reference.decode_fp8_e4m3(np.arange(0x80, 0xFF)), -pos)
+
+
+def test_fp8_encoder_round_trips_every_finite_code():
+    # The generator's encoder (its own table) and the oracle's decoder agree
+    # on every finite code, and the encoder picks the nearest code.
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = reference.decode_fp8_e4m3(codes)
+    assert np.array_equal(mla_synth.f32_to_fp8_e4m3_bits(vals)[1:], codes[1:])
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal(2000) * 30
+    enc = reference.decode_fp8_e4m3(mla_synth.f32_to_fp8_e4m3_bits(x))
+    finite = reference.decode_fp8_e4m3(codes)
+    nearest = np.min(np.abs(finite[None, :] - np.clip(x, -448, 448)[:, None]), axis=1)
+    assert np.all(np.abs(enc - np.clip(x, -448, 448)) == nearest)
+
+
+@pytest.mark.parametrize("contexts,block_size", [([1], 32), ([40], 32), ([33, 17], 16)])
+def test_fp8_latent_matches_brute_force(contexts, block_size):
+    # The 50-digit loops decode the bytes case by case, times the scale.
+    case = fp8_case(451 + contexts[0], contexts, block_size=block_size, poison=True)
+    assert case.ckv_pool.dtype == np.uint8
+    out, lse2 = oracle.latent_f64(case)
+    for b in range(case.batch):
+        for h in range(case.heads):
+            eo, el = _brute_errors(case, b, h, out, lse2)
+            assert eo < 1e-12 and el < 1e-12, (b, h, eo, el)
+
+
+def test_fp8_single_token_closed_form():
+    # One token: the output is that token's dequantized row exactly, and
+    # lse2 = scale * (qa . c + qp . k) * log2(e).
+    case = fp8_case(461, [1], heads=3, kv_scale=0.125)
+    out, lse2 = oracle.latent_f64(case)
+    phys = case.block_table[0, 0]
+    c = reference.decode_fp8_e4m3(case.ckv_pool[phys, 0]) * 0.125
+    k = reference.decode_fp8_e4m3(case.kpe_pool[phys, 0]) * 0.125
+    for h in range(3):
+        assert np.array_equal(out[0, h], c)
+        qa = reference.decode16(case.q_absorbed[0, h], case.dtype)
+        qp = reference.decode16(case.q_pe[0, h], case.dtype)
+        assert abs(lse2[0, h] - case.scale * (qa @ c + qp @ k) * reference.LOG2_E) < 1e-12
+
+
+def test_fp8_scale_is_linear_in_the_values():
+    # Doubling the scale doubles every dequantized value: the output doubles
+    # exactly when the queries are zero (uniform weights).
+    case = fp8_case(471, [70], heads=2)
+    case.q_absorbed[:] = 0
+    case.q_pe[:] = 0
+    a, la = oracle.latent_f64(case)
+    case.kv_scale *= 2
+    b, lb = oracle.latent_f64(case)
+    assert np.array_equal(b, 2 * a) and np.array_equal(la, lb)
+
+
+def test_fp8_wrong_exponent_bias_is_caught(monkeypatch):
+    # The other common E4M3 variant (bias 8, no negative zero) is a
+    # plausible mistake; the closed forms reject it.
+    def fnuz(bits):
+        b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+        e, m = (b >> 3) & 0xF, (b & 7).astype(np.float64)
+        mag = np.where(e == 0, m / 8.0 * 2.0 ** -7, (1.0 + m / 8.0) * np.exp2(e - 8.0))
+        return np.where(b >> 7, -mag, mag)
+    monkeypatch.setattr(reference, "decode_fp8_e4m3", fnuz)
+    with pytest.raises(AssertionError):
+        test_fp8_decode_closed_forms()
