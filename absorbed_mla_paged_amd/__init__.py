@@ -26,7 +26,8 @@ STATUS = {0: "MLA_OK", -1: "MLA_E_NULL", -2: "MLA_E_SHAPE", -3: "MLA_E_RANGE",
 
 # Every function include/mla_decode.h declares.
 EXPORTS = ["mla_default_plan_params", "mla_choose_partitions", "mla_partition_range",
-           "mla_decode_partition", "mla_decode_reduce", "mla_decode_fused", "mla_absorb_query",
+           "mla_decode_partition", "mla_decode_partition_fp8", "mla_decode_reduce",
+           "mla_decode_fused", "mla_absorb_query",
            "mla_unabsorb_output", "mla_status_string",
            "mla_last_error", "mla_get_counters", "mla_reset_counters"]
 
@@ -82,6 +83,10 @@ def load_library(path: str | None = None):
                                          ctypes.c_float, i32, vp, vp, vp, i32, i32, i32,
                                          vp, vp, vp, vp, vp, vp]
     lib.mla_decode_partition.restype = ctypes.c_int
+    lib.mla_decode_partition_fp8.argtypes = [vp, vp, vp, vp, ctypes.c_float, i32, i32, vp, i32,
+                                             vp, i32, i32, i32, ctypes.c_float, i32, vp, vp, vp,
+                                             i32, i32, i32, vp, vp, vp, vp, vp, vp]
+    lib.mla_decode_partition_fp8.restype = ctypes.c_int
     lib.mla_decode_reduce.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
     lib.mla_decode_reduce.restype = ctypes.c_int
     lib.mla_decode_fused.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, vp, i32, i32, i32,
@@ -241,6 +246,29 @@ def mla_decode_partition(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, co
         _ptr(partial_lse2), _ptr(out), _ptr(lse2_out), _ptr(debug_ranges), _stream(stream)))
 
 
+def mla_decode_partition_fp8(q_absorbed, q_pe, ckv_cache, kpe_cache, kv_scale: float,
+                             block_table, context_lens, scale: float, partitions, splits,
+                             row_indptr, total_rows: int, max_rows_per_req: int,
+                             heads_per_wg: int, partial_out, partial_lse2, out, lse2_out=None,
+                             debug_ranges=None, stream=None, q_len=None):
+    """The partition kernel over an E4M3 byte cache (uint8 tensors
+    [num_blocks, block_size, 512] and [.., 64]) times kv_scale (see
+    include/mla_decode.h). Plans must use 16 heads per workgroup."""
+    import torch
+    lib = load_library()
+    _need_cuda(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens)
+    if ckv_cache.dtype != torch.uint8 or kpe_cache.dtype != torch.uint8:
+        raise MlaError(-6, "E4M3 caches are passed as uint8 tensors")
+    B, H, Q = _query_shape(q_absorbed, q_len)
+    _check(lib.mla_decode_partition_fp8(
+        _ptr(q_absorbed), _ptr(q_pe), _ptr(ckv_cache), _ptr(kpe_cache), float(kv_scale),
+        int(ckv_cache.shape[0]), int(ckv_cache.shape[1]), _ptr(block_table),
+        int(block_table.shape[1]), _ptr(context_lens), B, H, Q, float(scale),
+        _dtype_code(q_absorbed), _ptr(partitions), _ptr(splits), _ptr(row_indptr),
+        int(total_rows), int(max_rows_per_req), int(heads_per_wg), _ptr(partial_out),
+        _ptr(partial_lse2), _ptr(out), _ptr(lse2_out), _ptr(debug_ranges), _stream(stream)))
+
+
 def mla_decode_fused(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens,
                      scale: float, partitions, splits, row_indptr, total_rows: int,
                      max_rows_per_req: int, heads_per_wg: int, partial_out, partial_lse2,
@@ -323,12 +351,30 @@ class DecodePlan:
 
 
 def decode(plan: DecodePlan, q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens,
-           scale: float, out, lse2_out=None, debug_ranges=None, stream=None, fused=False):
+           scale: float, out, lse2_out=None, debug_ranges=None, stream=None, fused=False,
+           kv_scale: float | None = None):
     """Partition launch, then the reduce launch when the plan needs one; with
-    fused=True, one launch that merges too."""
+    fused=True, one launch that merges too. uint8 caches are E4M3 bytes
+    times kv_scale (mla_decode_partition_fp8; the plan must use 16 heads per
+    workgroup)."""
     if int(ckv_cache.shape[1]) != plan.block_size:
         raise MlaError(-2, f"cache blocks of {int(ckv_cache.shape[1])} tokens, plan chosen for "
                            f"{plan.block_size}")
+    import torch
+    if ckv_cache.dtype == torch.uint8:
+        if fused:
+            raise MlaError(-6, "the fused launch takes 16-bit caches only")
+        mla_decode_partition_fp8(q_absorbed, q_pe, ckv_cache, kpe_cache,
+                                 1.0 if kv_scale is None else kv_scale, block_table,
+                                 context_lens, scale, plan.partitions, plan.splits,
+                                 plan.row_indptr, plan.total_rows, plan.info["max_rows_per_req"],
+                                 plan.info["heads_per_wg"], plan.partial_out, plan.partial_lse2,
+                                 out, lse2_out if not plan.info["needs_reduce"] else None,
+                                 debug_ranges, stream, q_len=plan.q_len)
+        if plan.info["needs_reduce"]:
+            mla_decode_reduce(plan.partial_out, plan.partial_lse2, plan.row_indptr, plan.batch,
+                              plan.q_len * plan.heads, plan.total_rows, out, lse2_out, stream)
+        return
     if fused:
         mla_decode_fused(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens, scale,
                          plan.partitions, plan.splits, plan.row_indptr, plan.total_rows,

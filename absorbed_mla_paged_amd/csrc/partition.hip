@@ -46,6 +46,12 @@
 //  * Outputs go out as device-scope write-through buffer stores, so the
 //    release at the end of the kernel has no dirty partial lines left to
 //    write back before the reduce can start.
+//  * Caches stored as E4M3 bytes (KV8): the copy waves load a stage's bytes
+//    into registers (half the bytes of a 16-bit stage), widen them to the
+//    16-bit type -- exactly, every E4M3 value is an fp16 and a bf16 value --
+//    and write them into the same swizzled LDS tile, so the compute waves
+//    run unchanged. The cache scale is folded into the score scale and into
+//    the output's normalisation.
 #include "fused_common.h"
 #include "partition_common.h"
 
@@ -75,10 +81,27 @@ static_assert(OPS_PER_COPY * 2 * 1024 == STAGE, "stage split");
 static_assert(OPS_PER_COPY < 64, "vmcnt range");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
+// Four E4M3 bytes of `w` -> four values of the 16-bit type DT, exactly,
+// as two packed words (byte i becomes element i).
+template <int DT> __device__ __forceinline__ u32x2 widen4(uint32_t w);
+template <> __device__ __forceinline__ u32x2 widen4<0>(uint32_t w) {
+  return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true))};
+}
+template <> __device__ __forceinline__ u32x2 widen4<1>(uint32_t w) {
+  return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))};
+}
+// Eight E4M3 bytes (w0 then w1) -> one 16-byte chunk of eight 16-bit values.
+template <int DT> __device__ __forceinline__ u32x4 widen8(uint32_t w0, uint32_t w1) {
+  const u32x2 a = widen4<DT>(w0), b = widen4<DT>(w1);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
 // The leading scalar kernel arguments (16 dwords, up to block_table) are
 // preloaded into SGPRs at wave launch on gfx950, so finding the row costs
 // no argument fetch; the PartitionArgs block is fetched meanwhile.
-template <int DT, bool FUSED, int PG>
+template <int DT, bool FUSED, int PG, bool KV8>
 __global__ __launch_bounds__(THREADS) void partition_kernel(
     int32_t groups, int32_t rows_per_req, int32_t slots, int32_t flags, int32_t total_rows,
     int32_t max_blocks, const int32_t* __restrict__ context_lens,
@@ -254,6 +277,91 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
     return;
   }
 
+  if (copier && KV8) {
+    // ---- copy waves, E4M3 cache: pair `slot` serves stages slot, slot + 2,
+    // ... Each wave loads its half of a stage's 36 KB of bytes into
+    // registers (18 one-KB loads: ops 0..31 are ckv rows 2 op and 2 op + 1,
+    // 32 lanes x 16 B each; ops 32..35 kpe rows 16 (op - 32) .. + 16, 4
+    // lanes each), issued before the slot is free; then widens them into the
+    // slot's 16-bit tile, zeros for rows past the range's end.
+    constexpr int OPS8 = ST_TOK * (LAT + ROPE) / 1024 / 2;   // 18
+    const int cw = wave - CWAVES;
+    const int slot = cw >> 1;
+    const int64_t tbl0 = (int64_t)b * max_blocks;
+    const int last_blk = a.num_blocks - 1;
+    const char* ckv8 = reinterpret_cast<const char*>(a.ckv);
+    const char* kpe8 = reinterpret_cast<const char*>(a.kpe);
+    MLA_LDS char* sb = smem + slot * STAGE;
+    struct Blocks {
+      int64_t p[NPG];
+    };
+    auto lookup = [&](int k) {
+      Blocks r;
+      const int nb_here = min(NPG, nblocks - NPG * k);
+#pragma unroll
+      for (int j = 0; j < NPG; ++j) {
+        const int blk = blk_lo + NPG * k + min(j, nb_here - 1);
+        const int v = __builtin_amdgcn_readfirstlane(load_const(block_table, tbl0 + blk));
+        r.p[j] = (int64_t)max(0, min(v, last_blk));
+      }
+      return r;
+    };
+    // The wave's half is a compile-time constant inside `run`, so every
+    // load's cache block is a fixed element of the lookup (no indexing).
+    auto run = [&](auto half_c) {
+      constexpr int half = decltype(half_c)::value;
+      Blocks phys_next = {};
+      if (slot < nst) phys_next = lookup(slot);
+      for (int k = slot, g = 0; k < nst; k += 2, ++g) {
+        const Blocks phys = phys_next;
+        if (k + 2 < nst) phys_next = lookup(k + 2);
+        wait_counter(issued, 2 * k);
+        u32x4 v[OPS8];
+#pragma unroll
+        for (int i = 0; i < OPS8; ++i) {
+          const int op = half * OPS8 + i;
+          const char* src;
+          if (op < ST_TOK / 2) {
+            const int r0 = 2 * op;   // both rows sit in one cache block
+            src = ckv8 + phys.p[r0 / PG] * (PG * LAT) + (r0 % PG + (lane >> 5)) * LAT + (lane & 31) * 16;
+          } else {
+            const int r0 = 16 * (op - ST_TOK / 2);
+            src = kpe8 + phys.p[r0 / PG] * (PG * ROPE) + (r0 % PG + (lane >> 2)) * ROPE +
+                  (lane & 3) * 16;
+          }
+          v[i] = *reinterpret_cast<const u32x4*>(src);
+        }
+        if (lane == 0) __hip_atomic_fetch_add(issued, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        wait_counter(freed + slot, CWAVES * g);
+        const int valid = min(ST_TOK, tok_hi - (tok_lo + k * ST_TOK));
+#pragma unroll
+        for (int i = 0; i < OPS8; ++i) {
+          const int op = half * OPS8 + i;
+          u32x4 e0 = widen8<DT>(v[i][0], v[i][1]);   // elements 0..7 of the lane's 16
+          u32x4 e1 = widen8<DT>(v[i][2], v[i][3]);   // elements 8..15
+          // Chunk c of a row sits at position c ^ swizzle(row).
+          if (op < ST_TOK / 2) {
+            const int r = 2 * op + (lane >> 5);
+            const int c = 2 * (lane & 31);
+            if (r >= valid) e0 = e1 = u32x4{0u, 0u, 0u, 0u};
+            *(MLA_LDS u32x4*)(sb + r * CKV_ROW + ((c ^ swz_ckv(r)) * 16)) = e0;
+            *(MLA_LDS u32x4*)(sb + r * CKV_ROW + (((c + 1) ^ swz_ckv(r)) * 16)) = e1;
+          } else {
+            const int r = 16 * (op - ST_TOK / 2) + (lane >> 2);
+            const int c = 2 * (lane & 3);
+            if (r >= valid) e0 = e1 = u32x4{0u, 0u, 0u, 0u};
+            *(MLA_LDS u32x4*)(sb + ST_KPE + r * KPE_ROW + ((c ^ swz_kpe(r)) * 16)) = e0;
+            *(MLA_LDS u32x4*)(sb + ST_KPE + r * KPE_ROW + (((c + 1) ^ swz_kpe(r)) * 16)) = e1;
+          }
+        }
+        bump_counter(ready + slot, lane);
+      }
+    };
+    if (cw & 1) run(std::integral_constant<int, 1>{});
+    else run(std::integral_constant<int, 0>{});
+    return;
+  }
+
   if (copier) {
     // ---- copy waves: pair `slot` serves stages slot, slot + 2, ... ------
     const int cw = wave - CWAVES;
@@ -363,7 +471,8 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
   auto finish = [&]() {
     float l_tot = l_part + shfl_xor(l_part, 16);
     l_tot = l_tot + shfl_xor(l_tot, 32);
-    const float inv = 1.0f / l_tot;
+    float inv = 1.0f / l_tot;
+    if constexpr (KV8) inv *= a.out_scale;
     const int dbase = wave * DT_PER_WAVE * 16 + lg * 4;
     const uint32_t e_off = (uint32_t)(ln * LAT + dbase);   // element offset in the region
     if (direct) {
@@ -541,7 +650,8 @@ using namespace mla;
 namespace {
 
 // Checks and launch shared by mla_decode_partition and mla_decode_fused.
-int partition_launch(bool fused, const void* q_absorbed, const void* q_pe, const void* ckv_cache,
+int partition_launch(bool fused, bool kv8, float kv_scale, const void* q_absorbed,
+                     const void* q_pe, const void* ckv_cache,
                      const void* kpe_cache, int32_t num_blocks, int32_t block_size,
                      const int32_t* block_table,
                      int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch,
@@ -559,10 +669,15 @@ int partition_launch(bool fused, const void* q_absorbed, const void* q_pe, const
   if (dtype != MLA_F16 && dtype != MLA_BF16) return fail(MLA_E_UNSUPPORTED, "dtype %d", dtype);
   if (q_len < 1 || q_len > MLA_MAX_QLEN)
     return fail(MLA_E_UNSUPPORTED, "q_len %d (need 1 .. %d)", q_len, MLA_MAX_QLEN);
-  const int32_t hpw = heads_per_wg ? heads_per_wg : default_heads_per_wg(num_heads);
+  const int32_t hpw = heads_per_wg ? heads_per_wg : (kv8 ? HG : default_heads_per_wg(num_heads));
   if (!valid_heads_per_wg(num_heads, hpw))
     return fail(MLA_E_UNSUPPORTED, "heads_per_wg %d for %d heads (16 or 64 dividing it)",
                 hpw, num_heads);
+  if (kv8 && hpw != HG)
+    return fail(MLA_E_UNSUPPORTED,
+                "E4M3 caches run 16 heads per workgroup (plan with heads_per_wg = 16), not %d", hpw);
+  if (kv8 && !(std::isfinite(kv_scale) && kv_scale > 0.0f))
+    return fail(MLA_E_RANGE, "kv_scale must be finite and > 0");
   if (!valid_block_size(block_size))
     return fail(MLA_E_UNSUPPORTED, "block_size %d (16 or 32 are supported)", block_size);
   if (!std::isfinite(scale)) return fail(MLA_E_RANGE, "scale is not finite");
@@ -619,6 +734,11 @@ int partition_launch(bool fused, const void* q_absorbed, const void* q_pe, const
   a.num_blocks = num_blocks;
   a.heads = qrows;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.out_scale = 1.0f;
+  if (kv8) {
+    a.scale_log2 *= kv_scale;
+    a.out_scale = kv_scale;
+  }
   const int32_t groups = qrows / hpw;
   const int32_t rows_per_req = direct ? 1 : max_rows_per_req;
 
@@ -636,16 +756,21 @@ int partition_launch(bool fused, const void* q_absorbed, const void* q_pe, const
   hipLaunchKernelGGL(K, grid, block, 0, stream, groups, rows_per_req, sl, dflag, total_rows, \
                      max_blocks_per_seq, context_lens, row_indptr, partitions, splits,       \
                      block_table, a)
-  else if (block_size == 16) {
-    if (dtype == MLA_F16 && merge_here) MLA_LAUNCH((partition_kernel<0, true, 16>));
-    else if (dtype == MLA_F16) MLA_LAUNCH((partition_kernel<0, false, 16>));
-    else if (merge_here) MLA_LAUNCH((partition_kernel<1, true, 16>));
-    else MLA_LAUNCH((partition_kernel<1, false, 16>));
+  else if (kv8) {
+    if (block_size == 16 && dtype == MLA_F16) MLA_LAUNCH((partition_kernel<0, false, 16, true>));
+    else if (block_size == 16) MLA_LAUNCH((partition_kernel<1, false, 16, true>));
+    else if (dtype == MLA_F16) MLA_LAUNCH((partition_kernel<0, false, 32, true>));
+    else MLA_LAUNCH((partition_kernel<1, false, 32, true>));
+  } else if (block_size == 16) {
+    if (dtype == MLA_F16 && merge_here) MLA_LAUNCH((partition_kernel<0, true, 16, false>));
+    else if (dtype == MLA_F16) MLA_LAUNCH((partition_kernel<0, false, 16, false>));
+    else if (merge_here) MLA_LAUNCH((partition_kernel<1, true, 16, false>));
+    else MLA_LAUNCH((partition_kernel<1, false, 16, false>));
   } else {
-    if (dtype == MLA_F16 && merge_here) MLA_LAUNCH((partition_kernel<0, true, 32>));
-    else if (dtype == MLA_F16) MLA_LAUNCH((partition_kernel<0, false, 32>));
-    else if (merge_here) MLA_LAUNCH((partition_kernel<1, true, 32>));
-    else MLA_LAUNCH((partition_kernel<1, false, 32>));
+    if (dtype == MLA_F16 && merge_here) MLA_LAUNCH((partition_kernel<0, true, 32, false>));
+    else if (dtype == MLA_F16) MLA_LAUNCH((partition_kernel<0, false, 32, false>));
+    else if (merge_here) MLA_LAUNCH((partition_kernel<1, true, 32, false>));
+    else MLA_LAUNCH((partition_kernel<1, false, 32, false>));
   }
 #undef MLA_LAUNCH
   const hipError_t e = hipGetLastError();
@@ -667,7 +792,8 @@ extern "C" int mla_decode_partition(
     int32_t total_rows, int32_t max_rows_per_req, int32_t heads_per_wg, float* partial_out,
     float* partial_lse2, void* out, float* lse2_out, int32_t* debug_ranges,
     hipStream_t stream) {
-  return partition_launch(false, q_absorbed, q_pe, ckv_cache, kpe_cache, num_blocks, block_size,
+  return partition_launch(false, false, 1.0f, q_absorbed, q_pe, ckv_cache, kpe_cache, num_blocks,
+                          block_size,
                           block_table,
                           max_blocks_per_seq, context_lens, batch, num_heads, q_len, scale, dtype,
                           partitions, splits, row_indptr, total_rows, max_rows_per_req,
@@ -685,10 +811,26 @@ extern "C" int mla_decode_fused(
     int32_t total_rows, int32_t max_rows_per_req, int32_t heads_per_wg, float* partial_out,
     float* partial_lse2, void* out, float* lse2_out, uint64_t* sync, int32_t* debug_ranges,
     hipStream_t stream) {
-  return partition_launch(true, q_absorbed, q_pe, ckv_cache, kpe_cache, num_blocks, block_size,
+  return partition_launch(true, false, 1.0f, q_absorbed, q_pe, ckv_cache, kpe_cache, num_blocks,
+                          block_size,
                           block_table,
                           max_blocks_per_seq, context_lens, batch, num_heads, q_len, scale, dtype,
                           partitions, splits, row_indptr, total_rows, max_rows_per_req,
                           heads_per_wg, partial_out, partial_lse2, out, lse2_out, sync,
                           debug_ranges, stream);
+}
+
+extern "C" int mla_decode_partition_fp8(
+    const void* q_absorbed, const void* q_pe, const void* ckv_cache, const void* kpe_cache,
+    float kv_scale, int32_t num_blocks, int32_t block_size, const int32_t* block_table,
+    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch, int32_t num_heads,
+    int32_t q_len, float scale, int32_t dtype, const int32_t* partitions, const int32_t* splits,
+    const int32_t* row_indptr, int32_t total_rows, int32_t max_rows_per_req,
+    int32_t heads_per_wg, float* partial_out, float* partial_lse2, void* out, float* lse2_out,
+    int32_t* debug_ranges, hipStream_t stream) {
+  return partition_launch(false, true, kv_scale, q_absorbed, q_pe, ckv_cache, kpe_cache,
+                          num_blocks, block_size, block_table, max_blocks_per_seq, context_lens,
+                          batch, num_heads, q_len, scale, dtype, partitions, splits, row_indptr,
+                          total_rows, max_rows_per_req, heads_per_wg, partial_out, partial_lse2,
+                          out, lse2_out, nullptr, debug_ranges, stream);
 }

@@ -24,7 +24,8 @@ struct PartitionArgs {
   uint64_t* sync;    // merge hand-off state (fused launches only)
   int32_t num_blocks;
   int32_t heads;     // query rows per request: q_len x heads of one new token
-  float scale_log2;  // scale * log2(e)
+  float scale_log2;  // scale * log2(e) (times the cache scale for E4M3 caches)
+  float out_scale;   // factor on the normalised output: the E4M3 cache scale, else 1
 };
 
 // The `flags` kernel argument (preloaded with the row lookup's arguments):

@@ -239,6 +239,38 @@ int mla_decode_partition(const void* q_absorbed, const void* q_pe, const void* c
                          int32_t* debug_ranges, hipStream_t stream);
 
 /*
+ * mla_decode_partition_fp8 -- the partition kernel over a latent cache
+ * stored as one byte per value.
+ *
+ * The same computation as mla_decode_partition, with every cached value
+ * (ckv and kpe alike) equal to its byte, read as E4M3 (the OCP 8-bit
+ * floating point format: exponent bias 7, 3 mantissa bits, largest value
+ * 448, S.1111.111 is NaN, no infinities), times kv_scale. Queries, outputs
+ * and partials are as in mla_decode_partition. The pages keep 16-bit caches
+ * only (mlxcel pull request 995 declines other cache modes); this layout,
+ * with one scale for the whole latent cache, is ours.
+ *
+ * Arguments as mla_decode_partition, except:
+ * ckv_cache   dev uint8 [num_blocks, block_size, 512], 16-byte aligned
+ * kpe_cache   dev uint8 [num_blocks, block_size, 64], 16-byte aligned
+ * kv_scale    the cache scale (finite, > 0; MLA_E_RANGE otherwise)
+ * dtype       the 16-bit type of q_absorbed, q_pe and out
+ * heads_per_wg must be 16 (or 0, which means 16 here): plan with
+ *             heads_per_wg = 16; MLA_E_UNSUPPORTED otherwise.
+ * Errors: as mla_decode_partition.
+ */
+int mla_decode_partition_fp8(const void* q_absorbed, const void* q_pe, const void* ckv_cache,
+                             const void* kpe_cache, float kv_scale, int32_t num_blocks,
+                             int32_t block_size, const int32_t* block_table,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens,
+                             int32_t batch, int32_t num_heads, int32_t q_len, float scale,
+                             int32_t dtype, const int32_t* partitions, const int32_t* splits,
+                             const int32_t* row_indptr, int32_t total_rows,
+                             int32_t max_rows_per_req, int32_t heads_per_wg, float* partial_out,
+                             float* partial_lse2, void* out, float* lse2_out,
+                             int32_t* debug_ranges, hipStream_t stream);
+
+/*
  * mla_decode_reduce -- the LSE-weighted reduce kernel (one launch).
  *
  * For each request b and query row h over rows r in [row_indptr[b],

@@ -57,7 +57,7 @@ def run_case(case, params: mla.PlanParams | None = None, dev=None, want_ranges=F
         ranges = torch.full((max(1, plan.total_rows), 2), -7, dtype=torch.int32, device="cuda")
     mla.decode(plan, dev["q_absorbed"], dev["q_pe"], dev["ckv_cache"], dev["kpe_cache"],
                dev["block_table"], dev["context_lens"], case.scale, out, lse2,
-               debug_ranges=ranges, fused=fused)
+               debug_ranges=ranges, fused=fused, kv_scale=dev.get("kv_scale"))
     torch.cuda.synchronize()
     o = out.float().cpu().numpy().astype(np.float64)
     l = lse2.cpu().numpy().astype(np.float64)

@@ -277,3 +277,30 @@ def test_decode_reduce_host_checks():
 def test_counters_reset():
     mla.mla_reset_counters()
     assert mla.mla_get_counters() == [0, 0, 0, 0]
+
+
+def test_decode_partition_fp8_host_checks_launch_nothing():
+    lib = mla.load_library()
+    vp = ctypes.c_void_p
+    good = vp(0x10000)
+
+    def call(**kw):
+        a = dict(qa=good, qp=good, ckv=good, kpe=good, ks=0.03125, nblk=4, bs=32, tbl=good,
+                 maxb=4, ctx=good, batch=1, heads=16, qlen=1, scale=0.07, dtype=0, P=good,
+                 S=good, ind=good, rows=2, maxr=2, hpw=16, po=good, pl=good, out=good, lo=None,
+                 dbg=None, stream=None)
+        a.update(kw)
+        return lib.mla_decode_partition_fp8(
+            a["qa"], a["qp"], a["ckv"], a["kpe"], a["ks"], a["nblk"], a["bs"], a["tbl"],
+            a["maxb"], a["ctx"], a["batch"], a["heads"], a["qlen"], a["scale"], a["dtype"],
+            a["P"], a["S"], a["ind"], a["rows"], a["maxr"], a["hpw"], a["po"], a["pl"],
+            a["out"], a["lo"], a["dbg"], a["stream"])
+    assert call(hpw=64, heads=128) == -6      # E4M3 caches run 16-head workgroups
+    assert call(ks=0.0) == -3
+    assert call(ks=-2.0) == -3
+    assert call(ks=float("inf")) == -3
+    assert call(bs=48) == -6
+    assert call(ckv=vp(0x10008)) == -4
+    assert call(kpe=None) == -1
+    assert call(dtype=3) == -6
+    assert call(batch=0) == 0
