@@ -49,15 +49,19 @@ MEASURED = {
     ("v2lite_32k", "6979dc04a8bc"): dict(fetch_kib=18631.0, write_kib=8208.0, mfma_busy=0.020),
     ("v2lite_32k@bs16", "6979dc04a8bc"): dict(fetch_kib=18638.0, write_kib=8208.0,
                                               mfma_busy=0.021),
+    # profiles/partition_kernel_v2lite_32k_fp8.md
+    ("v2lite_32k@fp8_e4m3", "6cd33c580a15"): dict(fetch_kib=9423.7, write_kib=8208.0,
+                                                  mfma_busy=0.023),
     # profiles/wide_kernel_v3_131k.md
     ("v3_131k", "cf00c39304d6"): dict(fetch_kib=74503.0, write_kib=32832.0, mfma_busy=0.282),
 }
 
 
-def workload_key(name: str, block_size: int) -> str:
-    """Key of the recorded counters: the workload, and the block size when
-    it is not 32."""
-    return name if block_size == 32 else f"{name}@bs{block_size}"
+def workload_key(name: str, block_size: int, kv_dtype=None) -> str:
+    """Key of the recorded counters: the workload, the block size when it is
+    not 32, and the cache storage when it is not 16-bit."""
+    key = name if block_size == 32 else f"{name}@bs{block_size}"
+    return key if kv_dtype is None else f"{key}@{kv_dtype}"
 
 
 def kernel_hash(hpw: int) -> str:
@@ -107,8 +111,10 @@ def log(*a):
 def algorithmic_bytes(case):
     """KV rows read + q read + out written + table and context lengths."""
     tokens = int(case.context_lens.astype(np.int64).sum())
-    nblk = int(sum((int(n) + 31) // 32 for n in case.context_lens))
-    kv = tokens * KV_BYTES_PER_TOKEN
+    bs = case.block_size
+    nblk = int(sum((int(n) + bs - 1) // bs for n in case.context_lens))
+    per_token = KV_BYTES_PER_TOKEN // 2 if case.kv_dtype == "fp8_e4m3" else KV_BYTES_PER_TOKEN
+    kv = tokens * per_token
     rows = case.batch * case.q_len * case.heads   # query rows: new tokens x heads
     q = rows * (512 + 64) * 2
     out = rows * 512 * 2
@@ -201,6 +207,9 @@ def main():
     ap.add_argument("--single-pass", action="store_true", help="force P = S = 1")
     ap.add_argument("--block-size", type=int, default=32, choices=(16, 32),
                     help="tokens per cache block of the paged layout")
+    ap.add_argument("--kv-fp8", action="store_true",
+                    help="latent cache stored as E4M3 bytes times a scale of 2^-5 "
+                         "(mla_decode_partition_fp8; 16-head workgroups)")
     ap.add_argument("--fused", action="store_true",
                     help="partition and merge in one launch (mla_decode_fused)")
     ap.add_argument("--projections", action="store_true",
@@ -235,7 +244,8 @@ def main():
     import mla_synth
 
     log(f"[bench] workload={args.workload} steps={args.steps} warmup={args.warmup}")
-    case = mla_synth.make_workload(args.workload, block_size=args.block_size)
+    fp8 = dict(kv_dtype="fp8_e4m3", kv_scale=2.0 ** -5) if args.kv_fp8 else {}
+    case = mla_synth.make_workload(args.workload, block_size=args.block_size, **fp8)
     if args.projections:
         projections(case, args, torch, mla)
         return
@@ -246,15 +256,22 @@ def main():
     def t16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(td).to(dev)
 
-    ckv = t16(case.ckv_pool)
-    kpe = t16(case.kpe_pool)
-    pool_bytes = ckv.numel() * 2 + kpe.numel() * 2
+    if args.kv_fp8:
+        ckv = torch.from_numpy(case.ckv_pool).to(dev)
+        kpe = torch.from_numpy(case.kpe_pool).to(dev)
+    else:
+        ckv = t16(case.ckv_pool)
+        kpe = t16(case.kpe_pool)
+    pool_bytes = ckv.numel() * ckv.element_size() + kpe.numel() * kpe.element_size()
     ncopy = max(1, min(64, math.ceil(args.cold_bytes / max(1, alg["kv"]))))
     copies = [(ckv, kpe)] + [(ckv.clone(), kpe.clone()) for _ in range(ncopy - 1)]
     qa, qp = t16(case.q_absorbed), t16(case.q_pe)
     table = torch.from_numpy(case.block_table).to(dev)
     ctx = torch.from_numpy(case.context_lens).to(dev)
     prm = mla.PlanParams(force_partitions=1, force_splits=1) if args.single_pass else None
+    if args.kv_fp8:
+        prm = prm or mla.PlanParams()
+        prm.heads_per_wg = 16
     plan = mla.DecodePlan(case.context_lens, case.heads, prm, device=dev, q_len=case.q_len,
                           block_size=case.block_size)
     qrows = case.q_len * case.heads
@@ -271,7 +288,8 @@ def main():
         mla.mla_choose_partitions(case.batch, case.heads, case.q_len, case.context_lens, prm,
                                   block_size=case.block_size)
         c, k = copies[j % ncopy]
-        mla.decode(plan, qa, qp, c, k, table, ctx, case.scale, out, lse2, fused=args.fused)
+        mla.decode(plan, qa, qp, c, k, table, ctx, case.scale, out, lse2, fused=args.fused,
+                   kv_scale=case.kv_scale)
 
     stream = torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
@@ -323,6 +341,13 @@ def main():
     with torch.cuda.graph(kgraph, stream=stream):
         for j in range(reps):
             c, k = copies[j % ncopy]
+            if args.kv_fp8:
+                mla.mla_decode_partition_fp8(qa, qp, c, k, case.kv_scale, table, ctx, case.scale,
+                                             plan.partitions, plan.splits, plan.row_indptr,
+                                             plan.total_rows, info["max_rows_per_req"],
+                                             info["heads_per_wg"], plan.partial_out,
+                                             plan.partial_lse2, out, lse2, q_len=plan.q_len)
+                continue
             mla.mla_decode_partition(qa, qp, c, k, table, ctx, case.scale, plan.partitions,
                                      plan.splits, plan.row_indptr, plan.total_rows,
                                      info["max_rows_per_req"], info["heads_per_wg"],
@@ -340,7 +365,7 @@ def main():
     split_bytes = info["total_rows"] * qrows * 513 * 4 if info["needs_reduce"] else 0
     pair_gbs = alg["total"] / (ms_per_step * 1e-3) / 1e9
     khash = kernel_hash(info["heads_per_wg"])
-    meas = MEASURED.get((workload_key(args.workload, case.block_size), khash))
+    meas = MEASURED.get((workload_key(args.workload, case.block_size, case.kv_dtype), khash))
     traffic = None
     if meas is not None:
         traffic = int(round((meas["fetch_kib"] * FETCH_SCALE + meas["write_kib"] * WRITE_SCALE) * 1024))
@@ -372,6 +397,7 @@ def main():
                    "q_len": case.q_len,
                    "context_lens": [int(n) for n in case.context_lens],
                    "block_size": case.block_size, "kv_lora_rank": 512, "rope_dim": 64,
+                   "kv_dtype": case.kv_dtype or case.dtype,
                    "plan": {"P": info["P"], "S": info["S"], "rows": info["total_rows"]},
                    "single_pass": bool(args.single_pass), "kv_copies": ncopy},
         "device_us": round(device_ms * 1e3, 3),
