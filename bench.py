@@ -328,6 +328,16 @@ def main():
         log("[bench] timed replay differs from the eager result")
         sys.exit(3)
     device_ms = gpu_ms / args.steps
+    # Four more replays of the same K steps, each timed on its own, so the
+    # spread across trials can be reported next to the timed run above.
+    trials_us = [round(device_ms * 1e3, 3)]
+    for _ in range(4):
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        trials_us.append(round(e0.elapsed_time(e1) * 1e3 / args.steps, 3))
     chooser_us = host_chooser_us(case, prm)
     # The step is the whole path: the host chooser, then the device work.
     ms_per_step = device_ms + chooser_us * 1e-3
@@ -335,7 +345,8 @@ def main():
         f"-> {device_ms * 1e3:.2f} us/step on the device + {chooser_us:.2f} us host chooser")
 
     # Partition kernel alone: back-to-back launches (rotating copies) in a
-    # graph, HIP events on the launch stream around them.
+    # graph, HIP events on the launch stream around them; the median of five
+    # replays.
     reps = args.kernel_reps
     kgraph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(kgraph, stream=stream):
@@ -355,12 +366,15 @@ def main():
                                      q_len=plan.q_len)
     kgraph.replay()
     torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        e0.record(stream)
-        kgraph.replay()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    part_us = e0.elapsed_time(e1) * 1e3 / reps
+    kernel_trials = []
+    for _ in range(5):
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            kgraph.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        kernel_trials.append(e0.elapsed_time(e1) * 1e3 / reps)
+    part_us = float(np.median(kernel_trials))
     achieved = alg["partition"] / (part_us * 1e-6) / 1e9
     split_bytes = info["total_rows"] * qrows * 513 * 4 if info["needs_reduce"] else 0
     pair_gbs = alg["total"] / (ms_per_step * 1e-3) / 1e9
@@ -401,6 +415,8 @@ def main():
                    "plan": {"P": info["P"], "S": info["S"], "rows": info["total_rows"]},
                    "single_pass": bool(args.single_pass), "kv_copies": ncopy},
         "device_us": round(device_ms * 1e3, 3),
+        "device_us_trials": {"median": float(np.median(trials_us)), "min": min(trials_us),
+                             "max": max(trials_us), "trials": trials_us},
         "host_chooser_us": round(chooser_us, 3),
         "achieved_gbs_pair": round(pair_gbs, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -409,6 +425,7 @@ def main():
                      "kernel": "partition_kernel" if info["heads_per_wg"] == 16 else "wide_kernel",
                      "kernel_source_hash": khash,
                      "kernel_us": round(part_us, 3),
+                     "kernel_us_trials": [round(t, 3) for t in kernel_trials],
                      "algorithmic_bytes": alg["partition"],
                      "mfma_busy": meas.get("mfma_busy") if meas else None},
         "cpu_baseline": cpu,
