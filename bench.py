@@ -8,8 +8,10 @@ LSE-weighted reduce. Inputs are synthetic and resident in HBM before timing
 starts. To keep the 256 MB Infinity Cache from serving repeated reads, each
 step reads a different copy of the KV pool (enough copies that the steps'
 working set is several times the cache). The K timed steps are captured into
-one HIP graph and replayed once between two HIP events, so host launch cost
-does not pad the figure.
+one HIP graph; after at least W untimed steps (whole replays of that graph)
+it is replayed once between two HIP events, so host launch cost does not pad
+the figure. More timed replays (--trials in all) give the spread across
+trials.
 
 Prints one JSON line on stdout (details on stderr). ``value`` is the decode
 latency in microseconds per step (lower is better). ``roofline`` is for the
@@ -202,7 +204,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=1000,
+                    help="untimed steps before the timed ones (run as whole replays of the "
+                         "K-step graph)")
     ap.add_argument("--workload", default="v2lite_32k")
     ap.add_argument("--single-pass", action="store_true", help="force P = S = 1")
     ap.add_argument("--block-size", type=int, default=32, choices=(16, 32),
@@ -220,6 +224,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=100)
+    ap.add_argument("--trials", type=int, default=5,
+                    help="timed replays of the step graph (the first one is `value`)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (for scaling "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -298,21 +304,32 @@ def main():
         step(0)
     torch.cuda.synchronize()
     eager = out.clone()
-    with torch.cuda.stream(stream):
-        for j in range(args.warmup):
-            step(j)
-    torch.cuda.synchronize()
 
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=stream):
         for j in range(args.steps):
             step(j)
     torch.cuda.synchronize()
-    graph.replay()            # untimed replay (also checks the graph result)
+    # Warm-up: untimed replays of the same K steps, at least W steps in all.
+    # Under sustained load the step time keeps falling for tens of ms (at
+    # V3 131K from 66 to 54 us per step over the first three replays of 200
+    # steps), so the timed run starts in that steady state.
+    warm_replays = max(1, math.ceil(args.warmup / max(1, args.steps)))
+    with torch.cuda.stream(stream):
+        for _ in range(warm_replays):
+            graph.replay()
     torch.cuda.synchronize()
     if not torch.equal(out, eager):
         log("[bench] graph replay differs from the eager result")
         sys.exit(3)
+    # The replay right after that check (a reduction and a read back to the
+    # host) runs slower at the large workloads (V3 131K: 67 against 57 us
+    # per step), so one more untimed replay separates the check from the
+    # timed run; the output is checked again after all timed replays.
+    with torch.cuda.stream(stream):
+        graph.replay()
+    torch.cuda.synchronize()
+    warmup_steps = (warm_replays + 1) * args.steps
 
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -324,20 +341,20 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = e0.elapsed_time(e1)
-    if not torch.equal(out, eager):
-        log("[bench] timed replay differs from the eager result")
-        sys.exit(3)
     device_ms = gpu_ms / args.steps
-    # Four more replays of the same K steps, each timed on its own, so the
-    # spread across trials can be reported next to the timed run above.
+    # More replays of the same K steps (--trials in all), each timed on its
+    # own, so the spread across trials is reported next to the timed run.
     trials_us = [round(device_ms * 1e3, 3)]
-    for _ in range(4):
+    for _ in range(args.trials - 1):
         with torch.cuda.stream(stream):
             e0.record(stream)
             graph.replay()
             e1.record(stream)
         torch.cuda.synchronize()
         trials_us.append(round(e0.elapsed_time(e1) * 1e3 / args.steps, 3))
+    if not torch.equal(out, eager):
+        log("[bench] timed replay differs from the eager result")
+        sys.exit(3)
     chooser_us = host_chooser_us(case, prm)
     # The step is the whole path: the host chooser, then the device work.
     ms_per_step = device_ms + chooser_us * 1e-3
@@ -400,7 +417,7 @@ def main():
         "unit": "us",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warmup_steps,
         "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": False,
         "scaling": "weak",
