@@ -121,8 +121,13 @@ def algorithmic_bytes(case):
     q = rows * (512 + 64) * 2
     out = rows * 512 * 2
     meta = nblk * 4 + case.batch * 4
+    # Score and value products: 2 * rows * (576 + 512) flops per visible
+    # token (new token j of a window sees n - q_len + 1 + j of them).
+    visible = sum(max(0, int(n) - case.q_len + 1 + j) for n in case.context_lens
+                  for j in range(case.q_len))
+    flops = 2 * case.heads * (576 + 512) * visible
     return dict(kv=kv, q=q, out=out, meta=meta, total=kv + q + out + meta,
-                partition=kv + q + meta, tokens=tokens)
+                partition=kv + q + meta, tokens=tokens, flops=flops)
 
 
 def cpu_baseline(case, budget_s: float):
@@ -394,6 +399,7 @@ def main():
     part_us = float(np.median(kernel_trials))
     achieved = alg["partition"] / (part_us * 1e-6) / 1e9
     split_bytes = info["total_rows"] * qrows * 513 * 4 if info["needs_reduce"] else 0
+    part_written = split_bytes if info["needs_reduce"] else alg["out"]
     pair_gbs = alg["total"] / (ms_per_step * 1e-3) / 1e9
     khash = kernel_hash(info["heads_per_wg"])
     meas = MEASURED.get((workload_key(args.workload, case.block_size, case.kv_dtype), khash))
@@ -444,6 +450,15 @@ def main():
                      "kernel_us": round(part_us, 3),
                      "kernel_us_trials": [round(t, 3) for t in kernel_trials],
                      "algorithmic_bytes": alg["partition"],
+                     # traffic against what the launch must move (KV, q and
+                     # table read, fp32 partials written); above 1.10 means
+                     # re-reads worth chasing
+                     "traffic_vs_algorithmic": (round(traffic / (alg["partition"] + part_written), 3)
+                                                if traffic else None),
+                     # time floors of one launch: its bytes at 8 TB/s and its
+                     # flops on 16-bit MFMA at 2.5 PFLOP/s (dense)
+                     "hbm_floor_us": round(alg["partition"] / (HBM_PEAK_GBS * 1e3), 3),
+                     "mfma_floor_us": round(alg["flops"] / 2.5e9, 3),
                      "mfma_busy": meas.get("mfma_busy") if meas else None},
         "cpu_baseline": cpu,
         "host": platform.node(),
