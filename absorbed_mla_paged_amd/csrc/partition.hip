@@ -200,6 +200,23 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
   MLA_LDS uint32_t* stored = ready + 6;  // compute waves: outputs stored (fused)
   MLA_LDS uint32_t* decided = ready + 7; // merge pieces known (fused)
   MLA_LDS int32_t* pieces = (MLA_LDS int32_t*)(ready + 8);   // first, count
+  // Copy waves read their first stage's block-table entries before the
+  // start-up barrier, so that round trip overlaps the other waves' arrival
+  // (a stage with fewer cache blocks than NPG repeats its last block).
+  int64_t first_phys[NPG] = {};
+  if (copier) {
+    const int slot0 = (wave - CWAVES) >> 1;
+    if (slot0 < nst) {
+      const int nb_here = min(NPG, nblocks - NPG * slot0);
+#pragma unroll
+      for (int j = 0; j < NPG; ++j) {
+        const int blk = blk_lo + NPG * slot0 + min(j, nb_here - 1);
+        const int v = __builtin_amdgcn_readfirstlane(
+            load_const(block_table, (int64_t)b * max_blocks + blk));
+        first_phys[j] = (int64_t)max(0, min(v, a.num_blocks - 1));
+      }
+    }
+  }
   if (tid < 8) ready[tid] = 0u;
   __syncthreads();
 
@@ -310,8 +327,9 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
     // load's cache block is a fixed element of the lookup (no indexing).
     auto run = [&](auto half_c) {
       constexpr int half = decltype(half_c)::value;
-      Blocks phys_next = {};
-      if (slot < nst) phys_next = lookup(slot);
+      Blocks phys_next;
+#pragma unroll
+      for (int j = 0; j < NPG; ++j) phys_next.p[j] = first_phys[j];   // stage `slot`
       for (int k = slot, g = 0; k < nst; k += 2, ++g) {
         const Blocks phys = phys_next;
         if (k + 2 < nst) phys_next = lookup(k + 2);
@@ -375,7 +393,8 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
     // Physical blocks of stage k (a stage with fewer cache blocks than
     // NPG copies its last block again, an L2 hit; those rows are either
     // never read or zeroed below). Looked up one stage ahead, so the
-    // block-table round trip overlaps the waits below.
+    // block-table round trip overlaps the waits below; the first stage's
+    // were read before the start-up barrier.
     auto lookup = [&](int k, int64_t* ph) {
       const int nb_here = min(NPG, nblocks - NPG * k);
 #pragma unroll
@@ -385,8 +404,9 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
         ph[j] = (int64_t)max(0, min(v, last_blk));
       }
     };
-    int64_t phys[NPG], phys_next[NPG] = {};
-    if (slot < nst) lookup(slot, phys_next);
+    int64_t phys[NPG], phys_next[NPG];
+#pragma unroll
+    for (int j = 0; j < NPG; ++j) phys_next[j] = first_phys[j];   // stage `slot`
     for (int k = slot, g = 0; k < nst; k += 2, ++g) {
 #pragma unroll
       for (int j = 0; j < NPG; ++j) phys[j] = phys_next[j];
