@@ -311,10 +311,16 @@ def main():
     eager = out.clone()
 
     graph = torch.cuda.CUDAGraph()
+    # The library counts launches on the host as they are made, so counters
+    # reset before the capture show which paths the K timed steps hold.
+    mla.mla_reset_counters()
     with torch.cuda.graph(graph, stream=stream):
         for j in range(args.steps):
             step(j)
     torch.cuda.synchronize()
+    c = mla.mla_get_counters()
+    path_counters = {"single_pass_launches": c[0], "split_launches": c[1],
+                     "reduce_launches": c[2], "rows_launched": c[3]}
     # Warm-up: untimed replays of the same K steps, at least W steps in all.
     # Under sustained load the step time keeps falling for tens of ms (at
     # V3 131K from 66 to 54 us per step over the first three replays of 200
@@ -435,8 +441,12 @@ def main():
                    "context_lens": [int(n) for n in case.context_lens],
                    "block_size": case.block_size, "kv_lora_rank": 512, "rope_dim": 64,
                    "kv_dtype": case.kv_dtype or case.dtype,
-                   "plan": {"P": info["P"], "S": info["S"], "rows": info["total_rows"]},
+                   "plan": {"P": info["P"], "S": info["S"], "rows": info["total_rows"],
+                            "heads_per_wg": info["heads_per_wg"], "groups": info["groups"],
+                            "tile_blocks": info["tile_blocks"],
+                            "needs_reduce": bool(info["needs_reduce"])},
                    "single_pass": bool(args.single_pass), "kv_copies": ncopy},
+        "path_counters": path_counters,
         "device_us": round(device_ms * 1e3, 3),
         "device_us_trials": {"median": float(np.median(trials_us)), "min": min(trials_us),
                              "max": max(trials_us), "trials": trials_us},
