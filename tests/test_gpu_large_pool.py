@@ -5,7 +5,8 @@ The small seeded case gives the oracle's answer. On the device its blocks are
 copied to block indices from BASE on, in a pool of BASE + pool blocks (the
 rest of the pool is left unwritten and is never read), and the block table
 is shifted by BASE. Both partition kernels (16 and 64 heads), both block
-sizes and the E4M3 cache are covered.
+sizes and the E4M3 cache are covered. A second test runs launches of several
+hundred requests, more workgroups than the chip holds at once.
 """
 import numpy as np
 import pytest
@@ -53,3 +54,27 @@ def test_blocks_past_4_gib(heads, block_size, fp8):
     compare(case, out, lse2, ref, lref, f"large pool H={heads} bs={block_size} fp8={fp8}")
     del ckv, kpe
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("batch,heads,block_size,fp8", [(600, 16, 32, False), (160, 128, 16, False),
+                                                        (300, 32, 32, True)])
+def test_large_batch(batch, heads, block_size, fp8):
+    # Many requests: the launch is not small, so the policy splits nothing
+    # (P = 1), and the grid holds more workgroups than the chip runs at once.
+    kw = dict(kv_dtype="fp8_e4m3", kv_scale=2.0 ** -5) if fp8 else {}
+    case = mla_synth.make_case(seed=902 + batch, batch=batch, heads=heads,
+                               context_range=(0, 2000), dtype="f16", block_size=block_size,
+                               poison=True, **kw)
+    log(f"[case] large batch B={batch} H={heads} bs={block_size} fp8={fp8}")
+    dev = to_device(case)
+    if fp8:
+        dev["ckv_cache"] = torch.from_numpy(case.ckv_pool).cuda()
+        dev["kpe_cache"] = torch.from_numpy(case.kpe_pool).cuda()
+        dev["kv_scale"] = case.kv_scale
+    prm = mla.PlanParams(heads_per_wg=16 if fp8 else 0)
+    out, lse2, plan, _ = run_case(case, prm, dev=dev)
+    workgroups = plan.total_rows * plan.info["groups"]
+    log(f"[plan] P max {max(plan.info['P'])}, rows {plan.total_rows}, {workgroups} workgroups")
+    assert max(plan.info["P"]) == 1 and workgroups > 256
+    ref, lref = oracle.latent_f64(case)
+    compare(case, out, lse2, ref, lref, f"large batch B={batch} H={heads} bs={block_size}")
