@@ -253,7 +253,7 @@ def mla_decode_partition_fp8(q_absorbed, q_pe, ckv_cache, kpe_cache, kv_scale: f
                              debug_ranges=None, stream=None, q_len=None):
     """The partition kernel over an E4M3 byte cache (uint8 tensors
     [num_blocks, block_size, 512] and [.., 64]) times kv_scale (see
-    include/mla_decode.h). Plans must use 16 heads per workgroup."""
+    include/mla_decode.h), with 16 or 64 heads per workgroup."""
     import torch
     lib = load_library()
     _need_cuda(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens)
@@ -355,8 +355,7 @@ def decode(plan: DecodePlan, q_absorbed, q_pe, ckv_cache, kpe_cache, block_table
            kv_scale: float | None = None):
     """Partition launch, then the reduce launch when the plan needs one; with
     fused=True, one launch that merges too. uint8 caches are E4M3 bytes
-    times kv_scale (mla_decode_partition_fp8; the plan must use 16 heads per
-    workgroup)."""
+    times kv_scale (mla_decode_partition_fp8)."""
     if int(ckv_cache.shape[1]) != plan.block_size:
         raise MlaError(-2, f"cache blocks of {int(ckv_cache.shape[1])} tokens, plan chosen for "
                            f"{plan.block_size}")

@@ -116,6 +116,19 @@ __device__ __forceinline__ u32x2 lds_read_tr_b16(uint32_t addr) {
   asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr) : "memory");
   return v;
 }
+__device__ __forceinline__ u32x2 lds_read_b64(uint32_t addr) {
+  u32x2 v;
+  asm volatile("ds_read_b64 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+// 8-bit transposing read: within each group of 16 lanes, lane j receives as
+// byte k (k = 0..7) byte j % 8 of the 8 bytes at the address of lane
+// 2 k + j / 8 of its group.
+__device__ __forceinline__ u32x2 lds_read_tr_b8(uint32_t addr) {
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
 // Wait until at most N LDS operations are outstanding; `v` (the value the
 // caller waits for) is routed through the statement so that its uses
 // cannot be scheduled above it.

@@ -81,23 +81,6 @@ static_assert(OPS_PER_COPY * 2 * 1024 == STAGE, "stage split");
 static_assert(OPS_PER_COPY < 64, "vmcnt range");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
-// Four E4M3 bytes of `w` -> four values of the 16-bit type DT, exactly,
-// as two packed words (byte i becomes element i).
-template <int DT> __device__ __forceinline__ u32x2 widen4(uint32_t w);
-template <> __device__ __forceinline__ u32x2 widen4<0>(uint32_t w) {
-  return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false)),
-               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true))};
-}
-template <> __device__ __forceinline__ u32x2 widen4<1>(uint32_t w) {
-  return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
-               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))};
-}
-// Eight E4M3 bytes (w0 then w1) -> one 16-byte chunk of eight 16-bit values.
-template <int DT> __device__ __forceinline__ u32x4 widen8(uint32_t w0, uint32_t w1) {
-  const u32x2 a = widen4<DT>(w0), b = widen4<DT>(w1);
-  return u32x4{a[0], a[1], b[0], b[1]};
-}
-
 // The leading scalar kernel arguments (16 dwords, up to block_table) are
 // preloaded into SGPRs at wave launch on gfx950, so finding the row costs
 // no argument fetch; the PartitionArgs block is fetched meanwhile.
@@ -689,13 +672,10 @@ int partition_launch(bool fused, bool kv8, float kv_scale, const void* q_absorbe
   if (dtype != MLA_F16 && dtype != MLA_BF16) return fail(MLA_E_UNSUPPORTED, "dtype %d", dtype);
   if (q_len < 1 || q_len > MLA_MAX_QLEN)
     return fail(MLA_E_UNSUPPORTED, "q_len %d (need 1 .. %d)", q_len, MLA_MAX_QLEN);
-  const int32_t hpw = heads_per_wg ? heads_per_wg : (kv8 ? HG : default_heads_per_wg(num_heads));
+  const int32_t hpw = heads_per_wg ? heads_per_wg : default_heads_per_wg(num_heads);
   if (!valid_heads_per_wg(num_heads, hpw))
     return fail(MLA_E_UNSUPPORTED, "heads_per_wg %d for %d heads (16 or 64 dividing it)",
                 hpw, num_heads);
-  if (kv8 && hpw != HG)
-    return fail(MLA_E_UNSUPPORTED,
-                "E4M3 caches run 16 heads per workgroup (plan with heads_per_wg = 16), not %d", hpw);
   if (kv8 && !(std::isfinite(kv_scale) && kv_scale > 0.0f))
     return fail(MLA_E_RANGE, "kv_scale must be finite and > 0");
   if (!valid_block_size(block_size))
@@ -769,7 +749,7 @@ int partition_launch(bool fused, bool kv8, float kv_scale, const void* q_absorbe
   const dim3 grid((unsigned)wgs), block(THREADS);
   const int32_t dflag = part::pack_flags(direct, q_len, num_heads), sl = (int32_t)slots;
   if (hpw != HG)
-    part::launch_wide(dtype, block_size, (unsigned)wgs, stream, groups, rows_per_req, sl, dflag,
+    part::launch_wide(dtype, block_size, kv8, (unsigned)wgs, stream, groups, rows_per_req, sl, dflag,
                       total_rows, max_blocks_per_seq, context_lens, row_indptr, partitions,
                       splits, block_table, a);
 #define MLA_LAUNCH(K)                                                                        \

@@ -140,6 +140,23 @@ __device__ __forceinline__ bool find_row(int b, int x, int direct, int total_row
   return true;
 }
 
+// Four E4M3 bytes of `w` -> four values of the 16-bit type DT, exactly,
+// as two packed words (byte i becomes element i).
+template <int DT> __device__ __forceinline__ dev::u32x2 widen4(uint32_t w);
+template <> __device__ __forceinline__ dev::u32x2 widen4<0>(uint32_t w) {
+  return dev::u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true))};
+}
+template <> __device__ __forceinline__ dev::u32x2 widen4<1>(uint32_t w) {
+  return dev::u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))};
+}
+// Eight E4M3 bytes (w0 then w1) -> one 16-byte chunk of eight 16-bit values.
+template <int DT> __device__ __forceinline__ dev::u32x4 widen8(uint32_t w0, uint32_t w1) {
+  const dev::u32x2 a = widen4<DT>(w0), b = widen4<DT>(w1);
+  return dev::u32x4{a[0], a[1], b[0], b[1]};
+}
+
 // Spin until the LDS counter reaches `target`. Every counter a wave waits on
 // is bumped by waves of the same (resident) workgroup that do not first
 // wait on this one, so the wait ends.
@@ -155,12 +172,12 @@ __device__ __forceinline__ void bump_counter(MLA_LDS uint32_t* c, int lane) {
 #endif  // __HIPCC__
 
 // Launch of the wide kernel (heads_per_wg 64); arguments as the 16-head
-// kernel's. Host side, after the launcher's checks.
-void launch_wide(int dtype, int block_size, unsigned wgs, hipStream_t stream, int32_t groups,
-                 int32_t rows_per_req, int32_t slots, int32_t flags, int32_t total_rows,
-                 int32_t max_blocks, const int32_t* context_lens, const int32_t* row_indptr,
-                 const int32_t* partitions, const int32_t* splits, const int32_t* block_table,
-                 const PartitionArgs& a);
+// kernel's, kv8 for E4M3 caches. Host side, after the launcher's checks.
+void launch_wide(int dtype, int block_size, bool kv8, unsigned wgs, hipStream_t stream,
+                 int32_t groups, int32_t rows_per_req, int32_t slots, int32_t flags,
+                 int32_t total_rows, int32_t max_blocks, const int32_t* context_lens,
+                 const int32_t* row_indptr, const int32_t* partitions, const int32_t* splits,
+                 const int32_t* block_table, const PartitionArgs& a);
 
 }  // namespace part
 }  // namespace mla

@@ -74,18 +74,42 @@ constexpr int DT_WAVE = LAT / 16 / 4;           // 8 output dim tiles per value 
 constexpr int HT_ALL = HPW / 16;                // 4 head tiles per workgroup
 constexpr int OPS = SEG + SEG * KPE_ROW / 1024; // 36 copy instructions per block
 constexpr int OPW = OPS / 4;                    // 9 per value wave
-constexpr int XP = NSLOT * SLOT;                // probabilities [parity][wave][lane] 16 B
-constexpr int XM = XP + 2 * NSC * 64 * 16;      // per-head floats [wave][2][16]
-constexpr int XFLAG = XM + NSC * 32 * 4;        // "second pass needed" flag
-constexpr int LDS_BYTES = XFLAG + 16;
+// E4M3 caches: the ring holds the cache bytes as stored (18 KB per block)
+// and the MFMA loops widen each fragment after reading it from LDS.
+constexpr int CKV_ROW8 = LAT;                        // 512 bytes
+constexpr int KPE_ROW8 = ROPE;                       // 64 bytes
+constexpr int SLOT8 = SEG * (CKV_ROW8 + KPE_ROW8);   // 18 KB per one-block slot
+constexpr int SLOT_KPE8 = SEG * CKV_ROW8;
+constexpr int OPW8 = 5;   // per value wave: 4 ckv copies of 2 rows, 8 kpe rows on 32 lanes
+constexpr int QBYTES = HPW * (CKV_ROW + KPE_ROW);    // the workgroup's Q, 72 KB
+// LDS layout: the ring of NSLOT slots, the Q staging from slot 2 on (idle
+// until step 0), then the probabilities [parity][wave][lane] 16 B, the
+// per-head floats [wave][2][16] and the "second pass needed" flag.
+template <bool KV8> struct Lds {
+  static constexpr int slot = KV8 ? SLOT8 : SLOT;
+  static constexpr int q = 2 * slot;
+  static constexpr int xp = q + QBYTES > NSLOT * slot ? q + QBYTES : NSLOT * slot;
+  static constexpr int xm = xp + 2 * NSC * 64 * 16;
+  static constexpr int flag = xm + NSC * 32 * 4;
+  static constexpr int bytes = flag + 16;
+  static_assert(bytes <= 160 * 1024, "LDS budget");
+};
 constexpr float HEADROOM_LOG2 = 15.0f;          // p <= 2^15 against the reference
 // LDS fragments read ahead in the score and value MFMA loops (at most 15
 // LDS reads may be in flight: the lgkmcnt field has 4 bits).
 constexpr int KD_SCORE = 8;
 constexpr int VD_VALUE = 5;
 static_assert(KD_SCORE <= 15 && 4 + 2 * VD_VALUE <= 15, "lgkmcnt range");
-static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-static_assert(OPS % 4 == 0 && 3 * OPW < 64, "copy split / vmcnt range");
+static_assert(OPS % 4 == 0 && 3 * OPW < 64 && 3 * OPW8 < 64, "copy split / vmcnt range");
+static_assert(4 * 4 * 2 * CKV_ROW8 == SLOT_KPE8 && 4 * 8 * KPE_ROW8 == SEG * KPE_ROW8,
+              "E4M3 copy split: 4 x 4 two-row ckv copies and 4 x 8 kpe rows per block");
+
+// E4M3 rows: chunk c (16 bytes) of ckv row r sits at c ^ swz8_ckv(r) (32
+// chunks, the low 4 bits permuted), of kpe row r at c ^ swz8_kpe(r) (4
+// chunks). 16 consecutive rows of either 16-token half, and the rows
+// {0..7, 16..23} or {8..15, 24..31}, each take 16 distinct bank groups.
+__device__ __forceinline__ int swz8_ckv(int r) { return (r & 15) ^ (((r >> 4) & 1) << 3); }
+__device__ __forceinline__ int swz8_kpe(int r) { return (r >> 2) & 3; }
 
 // Two probabilities rounded (to nearest even) into the 16-bit type, packed
 // low / high; and the sum of such a pair added to an fp32 total (one dot2
@@ -120,12 +144,14 @@ struct Phys {
 
 // Wait until at most `later` blocks' worth of this wave's copies are still
 // in flight (copies complete in issue order).
+// W is the number of copy instructions per block and wave.
+template <int W>
 __device__ __forceinline__ void wait_blocks(int later) {
   switch (later) {
     case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<OPW>(); break;
-    case 2: wait_vmcnt<2 * OPW>(); break;
-    default: wait_vmcnt<3 * OPW>(); break;
+    case 1: wait_vmcnt<W>(); break;
+    case 2: wait_vmcnt<2 * W>(); break;
+    default: wait_vmcnt<3 * W>(); break;
   }
 }
 
@@ -139,7 +165,9 @@ __device__ __forceinline__ void meet() {
 
 // A "block" below is one 32-token segment of the row: one cache block of
 // PG = 32 tokens, or two of PG = 16 (looked up separately in the table).
-template <int DT, int PG>
+// KV8: the cache holds E4M3 bytes (times the one scale folded into
+// scale_log2 and out_scale).
+template <int DT, int PG, bool KV8>
 __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
     int32_t groups, int32_t rows_per_req, int32_t slots, int32_t flags, int32_t total_rows,
     int32_t max_blocks, const int32_t* __restrict__ context_lens,
@@ -151,8 +179,10 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
   typedef typename E::vec4 vec4;
   typedef typename E::scalar scalar;
   typedef Prob<DT> P;
+  typedef Lds<KV8> L;
+  constexpr int OPWK = KV8 ? OPW8 : OPW;   // copy instructions per block and value wave
 
-  __shared__ __attribute__((aligned(1024))) char smem_raw[LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[L::bytes];
   MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -244,13 +274,31 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
   // op 9 sw + i; ops 0..31 are ckv rows, 32..35 kpe rows 8 (op - 32) .. + 8.
   // Chunk c of an LDS row sits at position c ^ swizzle(row).
   auto issue_one = [&](int k, const Phys& ph, int i) {
-    const uint32_t base = lds0 + (k & (NSLOT - 1)) * SLOT;
+    const uint32_t base = lds0 + (k & (NSLOT - 1)) * L::slot;
     const int op = sw * OPW + i;
     // The lane offsets are recomputed per copy from an opaque lane index:
     // hoisted out of the step loop they would hold registers throughout it.
     int lane;
     asm volatile("v_mov_b32 %0, %1" : "=v"(lane) : "v"(lane_id));
-    if (op < SEG) {
+    if constexpr (KV8) {
+      // E4M3: copies 0..3 of value wave sw are ckv rows 2 o and 2 o + 1
+      // (o = 4 sw + i; 32 lanes of 16 bytes each), copy 4 its kpe rows
+      // 8 sw .. + 8 on lanes 0..31.
+      if (i < 4) {
+        const int o = 4 * sw + i;
+        const int r = 2 * o + (lane >> 5);
+        const uint32_t voff = (lane >> 5) * CKV_ROW8 + ((lane & 31) ^ swz8_ckv(r)) * 16;
+        const int64_t pj = (PG == SEG || 2 * o < PG) ? ph.p[0] : ph.p[1];   // wave-uniform
+        dma16s(voff, ckv_base + pj * (PG * CKV_ROW8) + ((2 * o) % PG) * CKV_ROW8,
+               base + o * 2 * CKV_ROW8);
+      } else if (lane < 32) {
+        const int r = 8 * sw + (lane >> 2);
+        const uint32_t voff = (lane >> 2) * KPE_ROW8 + ((lane & 3) ^ swz8_kpe(r)) * 16;
+        const int64_t pj = (PG == SEG || 8 * sw < PG) ? ph.p[0] : ph.p[1];
+        dma16s(voff, kpe_base + pj * (PG * KPE_ROW8) + ((8 * sw) % PG) * KPE_ROW8,
+               base + SLOT_KPE8 + 8 * sw * KPE_ROW8);
+      }
+    } else if (op < SEG) {
       // ckv row op: row op % PG of cache block op / PG of the segment.
       const uint32_t voff = ((lane & ~15) | ((lane & 15) ^ swz_ckv(op))) * 16;
       const int64_t pj = (PG == SEG || op < PG) ? ph.p[0] : ph.p[1];   // wave-uniform
@@ -272,9 +320,15 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
   auto zero_tail = [&](int k) {
     const int valid = min(SEG, ntok_all - k * SEG);
     if (valid < SEG) {
-      for (int r = max(valid, sw * OPW); r < min(SEG, (sw + 1) * OPW); ++r)
-        *(MLA_LDS u32x4*)(smem + (k & (NSLOT - 1)) * SLOT + r * CKV_ROW + lane * 16) =
-            u32x4{0u, 0u, 0u, 0u};
+      if constexpr (KV8) {
+        for (int r = max(valid, 8 * sw); r < 8 * sw + 8; ++r)
+          *(MLA_LDS u32x2*)(smem + (k & (NSLOT - 1)) * L::slot + r * CKV_ROW8 + lane * 8) =
+              u32x2{0u, 0u};
+      } else {
+        for (int r = max(valid, sw * OPW); r < min(SEG, (sw + 1) * OPW); ++r)
+          *(MLA_LDS u32x4*)(smem + (k & (NSLOT - 1)) * L::slot + r * CKV_ROW + lane * 16) =
+              u32x4{0u, 0u, 0u, 0u};
+      }
     }
   };
 
@@ -286,7 +340,7 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
       const Phys ph = next;
       if (i + 3 < nblocks) next = phys_of(i + 3);
 #pragma unroll
-      for (int c = 0; c < OPW; ++c) issue_one(i + 2, ph, c);
+      for (int c = 0; c < OPWK; ++c) issue_one(i + 2, ph, c);
     }
   };
 
@@ -296,9 +350,9 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
   // Loaded per score wave straight from memory it would cost every CU
   // 144 KB (two waves share each head), twice the first two KV blocks.
   // Rows are swizzled like the KV rows.
-  const uint32_t qlds = lds0 + 2 * SLOT;
-  static_assert(HPW * (CKV_ROW + KPE_ROW) == 2 * SLOT && 8 * OPW == HPW + HPW * KPE_ROW / 1024,
-                "Q staging fills slots 2 and 3 in 8 x 9 copies");
+  const uint32_t qlds = lds0 + L::q;
+  static_assert(QBYTES == 2 * SLOT && 8 * OPW == HPW + HPW * KPE_ROW / 1024,
+                "Q staging: 72 KB in 8 x 9 copies");
   auto issue_q = [&]() {
     const int64_t q0 = (int64_t)b * a.heads + hwg;
     const char* qa_base = reinterpret_cast<const char*>(a.q_absorbed + q0 * LAT);
@@ -320,8 +374,8 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
     }
   };
 
-  MLA_LDS float* xm = (MLA_LDS float*)(smem + XM);   // [score wave][j][ln]
-  MLA_LDS uint32_t* flag = (MLA_LDS uint32_t*)(smem + XFLAG);
+  MLA_LDS float* xm = (MLA_LDS float*)(smem + L::xm);   // [score wave][j][ln]
+  MLA_LDS uint32_t* flag = (MLA_LDS uint32_t*)(smem + L::flag);
   if (tid == 0) *flag = 0u;   // seen by all after the first meeting below
 
   const float c2 = a.scale_log2;
@@ -380,13 +434,21 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
     // Loop-invariant LDS byte offsets inside a slot. Score fragment (K-step
     // ks): row 16 tt + ln, chunk 4 ks + lg; chunks 16 apart keep the same
     // swizzled low bits, so ks = 4 m + kk is offs_k[kk] + 256 m.
+    // E4M3 fragment (K-step ks): the 8 bytes of row 16 tt + ln at byte
+    // 32 ks + 8 lg, i.e. half lg % 2 of chunk 2 ks + lg / 2; chunks 16 apart
+    // keep the same swizzled low bits, so ks = 8 m + kk is offs_k[kk] + 256 m.
     const int rk = 16 * tt + ln;
-    uint32_t offs_k[4], offs_p[2];
+    constexpr int NOFF = KV8 ? 8 : 4;
+    uint32_t offs_k[NOFF], offs_p[2];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) offs_k[kk] = rk * CKV_ROW + (((4 * kk + lg) ^ swz_ckv(rk)) * 16);
+    for (int kk = 0; kk < NOFF; ++kk)
+      offs_k[kk] = KV8 ? rk * CKV_ROW8 + (((2 * kk + (lg >> 1)) ^ swz8_ckv(rk)) * 16) + (lg & 1) * 8
+                       : rk * CKV_ROW + (((4 * kk + lg) ^ swz_ckv(rk)) * 16);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
-      offs_p[kk] = SLOT_KPE + rk * KPE_ROW + (((4 * kk + lg) ^ swz_kpe(rk)) * 16);
+      offs_p[kk] = KV8 ? SLOT_KPE8 + rk * KPE_ROW8 +
+                             (((2 * kk + (lg >> 1)) ^ swz8_kpe(rk)) * 16) + (lg & 1) * 8
+                       : SLOT_KPE + rk * KPE_ROW + (((4 * kk + lg) ^ swz_kpe(rk)) * 16);
     float m_ref[2] = {-INFINITY, -INFINITY};  // reference maxima of my heads (scaled)
     float m_run[2] = {-INFINITY, -INFINITY};  // max of this lane's own raw scores
     float l_part[2] = {0.f, 0.f};             // this lane's share of the sums
@@ -396,25 +458,37 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
         meet();   // M_step(i): block i is in LDS; P(i - 2)'s buffer is free
         if (i >= nblocks) continue;
         // ---- scores: my 16 tokens x 32 heads of block i -----------------------
-        const uint32_t sbase = lds0 + (i & (NSLOT - 1)) * SLOT;
+        const uint32_t sbase = lds0 + (i & (NSLOT - 1)) * L::slot;
         const int valid = min(SEG, ntok - i * SEG);
         auto kaddr = [&](int ks) {
-          return sbase + ((ks < LAT / 32) ? offs_k[ks & 3] + 256 * (ks >> 2)
+          return sbase + ((ks < LAT / 32) ? offs_k[ks % NOFF] + 256 * (ks / NOFF)
                                           : offs_p[ks - LAT / 32]);
+        };
+        // A K fragment as read from LDS (8 E4M3 bytes, or 8 16-bit values)
+        // and as the MFMA takes it.
+        using KRaw = std::conditional_t<KV8, u32x2, vec8>;
+        auto kread = [&](int ks) -> KRaw {
+          if constexpr (KV8) return lds_read_b64(kaddr(ks));
+          else return lds_read_b128<vec8>(kaddr(ks));
+        };
+        auto kwide = [&](const KRaw& r) -> vec8 {
+          if constexpr (KV8) return __builtin_bit_cast(vec8, widen8<DT>(r[0], r[1]));
+          else return r;
         };
         constexpr int KD = KD_SCORE;
         f32x4 acc[2][2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        vec8 kf[KSTEPS];
+        KRaw kf[KSTEPS];
 #pragma unroll
-        for (int ks = 0; ks < KD; ++ks) kf[ks] = lds_read_b128<vec8>(kaddr(ks));
+        for (int ks = 0; ks < KD; ++ks) kf[ks] = kread(ks);
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
           lds_wait_n(min(KD - 1, KSTEPS - 1 - ks), kf[ks]);   // reads issued after ks
-          acc[0][ks & 1] = E::mfma(kf[ks], qfrag(0, ks), acc[0][ks & 1]);
-          acc[1][ks & 1] = E::mfma(kf[ks], qfrag(1, ks), acc[1][ks & 1]);
-          if (ks + KD < KSTEPS) kf[ks + KD] = lds_read_b128<vec8>(kaddr(ks + KD));
+          const vec8 kv = kwide(kf[ks]);
+          acc[0][ks & 1] = E::mfma(kv, qfrag(0, ks), acc[0][ks & 1]);
+          acc[1][ks & 1] = E::mfma(kv, qfrag(1, ks), acc[1][ks & 1]);
+          if (ks + KD < KSTEPS) kf[ks + KD] = kread(ks + KD);
           // Keep the MFMAs between their waits: sunk below later waits they
           // would stop overlapping the reads.
           __builtin_amdgcn_sched_barrier(0);
@@ -467,7 +541,7 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
           pme[2 * j + 1] = P::pack2(pf[2], pf[3]);
           l_part[j] = P::sum2(pme[2 * j + 1], P::sum2(pme[2 * j], l_part[j]));
         }
-        *(MLA_LDS u32x4*)(smem + XP + (((i & 1) * NSC + sw) * 64 + lane) * 16) = pme;
+        *(MLA_LDS u32x4*)(smem + L::xp + (((i & 1) * NSC + sw) * 64 + lane) * 16) = pme;
       }
       if (pass == 1) break;
       // Did any score outgrow its head's reference?
@@ -517,35 +591,54 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
   // i.e. at 16 sw + 2 (d ^ (swz / 2)) + ((ln / 2) ^ swz) % 2. They are
   // rebuilt each step from an opaque copy of swz (three VALU operations per
   // fragment) instead of being held in eight registers.
+  //
+  // E4M3: fragment d is one 8-bit transposing read. Lanes 2 k and 2 k + 1
+  // of a 16-lane group address the two 8-byte halves of dims 16 (8 sw + d)
+  // .. + 16 of token T_k (4 lg + k, then 16 + 4 lg + k - 4: the token order
+  // of the P^T operand), so lane ln receives dim 16 (8 sw + d) + ln of
+  // tokens T_0 .. T_7, the A-operand layout. Chunk 8 sw + d of row T sits at
+  // ((8 sw) ^ (swz & 8)) + (d ^ (swz & 7)).
   const int r1 = 4 * lg + (ln >> 2);
-  const int swz_v = swz_ckv(r1);
-  const uint32_t vrow = r1 * CKV_ROW + (16 * sw + (((ln >> 1) ^ swz_v) & 1)) * 16 + (ln & 1) * 8;
+  const int t8 = (ln >> 1) < 4 ? 4 * lg + (ln >> 1) : 12 + 4 * lg + (ln >> 1);
+  const int swz_v = KV8 ? swz8_ckv(t8) : swz_ckv(r1);
+  const uint32_t vrow =
+      KV8 ? t8 * CKV_ROW8 + ((8 * sw) ^ (swz_v & 8)) * 16 + (ln & 1) * 8
+          : r1 * CKV_ROW + (16 * sw + (((ln >> 1) ^ swz_v) & 1)) * 16 + (ln & 1) * 8;
   f32x4 o[DT_WAVE][HT_ALL];
   // Block kb's values into o. The first block of a pass starts the
   // accumulators from a zero C operand instead of a separate zeroing (which
   // the compiler would keep apart from the accumulators and copy around).
   auto apply = [&](int kb, auto first_block) {
     constexpr bool first = decltype(first_block)::value;
-    const uint32_t sbase = lds0 + (kb & (NSLOT - 1)) * SLOT;
+    const uint32_t sbase = lds0 + (kb & (NSLOT - 1)) * L::slot;
     int sh;
-    asm volatile("v_lshrrev_b32 %0, 1, %1" : "=v"(sh) : "v"(swz_v));   // swz / 2, opaque
+    if constexpr (KV8)
+      asm volatile("v_and_b32 %0, 7, %1" : "=v"(sh) : "v"(swz_v));        // swz & 7, opaque
+    else
+      asm volatile("v_lshrrev_b32 %0, 1, %1" : "=v"(sh) : "v"(swz_v));   // swz / 2, opaque
     const uint32_t vbase = sbase + vrow;
-    auto vaddr = [&](int d) { return vbase + 32u * (uint32_t)(d ^ sh); };
+    auto vaddr = [&](int d) { return vbase + (KV8 ? 16u : 32u) * (uint32_t)(d ^ sh); };
     // P^T B operand of head tile ht (pair ht / 2, tile ht % 2): tokens
     // 4 lg + e from score wave ht / 2, 16 + 4 lg + e from score wave ht / 2 + 2.
-    const uint32_t pbase = lds0 + XP + ((kb & 1) * NSC * 64 + lane) * 16;
+    const uint32_t pbase = lds0 + L::xp + ((kb & 1) * NSC * 64 + lane) * 16;
     u32x4 pw[NSC];
 #pragma unroll
     for (int v = 0; v < NSC; ++v) pw[v] = lds_read_b128<u32x4>(pbase + v * 64 * 16);
     constexpr int VD = VD_VALUE;
+    constexpr int RPF = KV8 ? 1 : 2;   // LDS reads per fragment
     u32x2 vr[DT_WAVE][2];
+    auto vread = [&](int d) {
+      if constexpr (KV8) {
+        vr[d][0] = lds_read_tr_b8(vaddr(d));
+      } else {
+        vr[d][0] = lds_read_tr_b16(vaddr(d));
+        vr[d][1] = lds_read_tr_b16(vaddr(d) + 16 * CKV_ROW);
+      }
+    };
 #pragma unroll
-    for (int d = 0; d < VD; ++d) {
-      vr[d][0] = lds_read_tr_b16(vaddr(d));
-      vr[d][1] = lds_read_tr_b16(vaddr(d) + 16 * CKV_ROW);
-    }
-    lds_wait<2 * VD>(pw[0], pw[1]);
-    lds_wait<2 * VD>(pw[2], pw[3]);
+    for (int d = 0; d < VD; ++d) vread(d);
+    lds_wait<RPF * VD>(pw[0], pw[1]);
+    lds_wait<RPF * VD>(pw[2], pw[3]);
     vec8 pv[HT_ALL];
 #pragma unroll
     for (int ht = 0; ht < HT_ALL; ++ht) {
@@ -556,16 +649,18 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
 #pragma unroll
     for (int d = 0; d < DT_WAVE; ++d) {
       // Reads issued after fragment d: fragments d+1 .. min(d+VD-1, 7).
-      lds_wait_n(2 * min(VD - 1, DT_WAVE - 1 - d), vr[d][0], vr[d][1]);
-      const vec8 va =
-          __builtin_bit_cast(vec8, u32x4{vr[d][0][0], vr[d][0][1], vr[d][1][0], vr[d][1][1]});
+      vec8 va;
+      if constexpr (KV8) {
+        lds_wait_n(min(VD - 1, DT_WAVE - 1 - d), vr[d][0]);
+        va = __builtin_bit_cast(vec8, widen8<DT>(vr[d][0][0], vr[d][0][1]));
+      } else {
+        lds_wait_n(2 * min(VD - 1, DT_WAVE - 1 - d), vr[d][0], vr[d][1]);
+        va = __builtin_bit_cast(vec8, u32x4{vr[d][0][0], vr[d][0][1], vr[d][1][0], vr[d][1][1]});
+      }
 #pragma unroll
       for (int ht = 0; ht < HT_ALL; ++ht)
         o[d][ht] = E::mfma(va, pv[ht], first ? f32x4{0.f, 0.f, 0.f, 0.f} : o[d][ht]);
-      if (d + VD < DT_WAVE) {
-        vr[d + VD][0] = lds_read_tr_b16(vaddr(d + VD));
-        vr[d + VD][1] = lds_read_tr_b16(vaddr(d + VD) + 16 * CKV_ROW);
-      }
+      if (d + VD < DT_WAVE) vread(d + VD);
       __builtin_amdgcn_sched_barrier(0);   // as in the score loop
     }
   };
@@ -576,10 +671,10 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
     for (int k = 0; k < npro; ++k) {
       const Phys ph = phys_of(k);
 #pragma unroll
-      for (int c = 0; c < OPW; ++c) issue_one(k, ph, c);
+      for (int c = 0; c < OPWK; ++c) issue_one(k, ph, c);
     }
     if (pass == 0) {
-      wait_blocks(npro);   // my part of Q has landed (the block copies may not have)
+      wait_blocks<OPWK>(npro);   // my part of Q has landed (the block copies may not have)
       meet();              // M_q
     }
     // Start of step i: block i must be in LDS (my later copies, of blocks
@@ -589,7 +684,7 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
     auto step_begin = [&](int i) {
       if (i < nblocks) {
         const int last = min(max(npro - 1, i + 1), nblocks - 1);
-        wait_blocks(last - i);
+        wait_blocks<OPWK>(last - i);
         if (i == nblocks - 1) zero_tail(i);
       }
       meet();
@@ -616,7 +711,8 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
   for (int ht = 0; ht < HT_ALL; ++ht) {
     const int w0 = ht >> 1, j = ht & 1;   // score waves w0 and w0 + 2
     const float l = xm[(w0 * 2 + j) * 16 + ln] + xm[((w0 + 2) * 2 + j) * 16 + ln];
-    const float inv = 1.0f / l;
+    float inv = 1.0f / l;
+    if constexpr (KV8) inv *= a.out_scale;
 #pragma unroll
     for (int d = 0; d < DT_WAVE; ++d) store(ht, sw * DT_WAVE + d, o[d][ht] * inv);
   }
@@ -624,13 +720,20 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
 
 }  // namespace
 
-void launch_wide(int dtype, int block_size, unsigned wgs, hipStream_t stream, int32_t groups,
-                 int32_t rows_per_req, int32_t slots, int32_t flags, int32_t total_rows,
-                 int32_t max_blocks, const int32_t* context_lens, const int32_t* row_indptr,
-                 const int32_t* partitions, const int32_t* splits, const int32_t* block_table,
-                 const PartitionArgs& a) {
-  auto kernel = dtype == MLA_F16 ? (block_size == 16 ? wide_kernel<0, 16> : wide_kernel<0, 32>)
-                                 : (block_size == 16 ? wide_kernel<1, 16> : wide_kernel<1, 32>);
+void launch_wide(int dtype, int block_size, bool kv8, unsigned wgs, hipStream_t stream,
+                 int32_t groups, int32_t rows_per_req, int32_t slots, int32_t flags,
+                 int32_t total_rows, int32_t max_blocks, const int32_t* context_lens,
+                 const int32_t* row_indptr, const int32_t* partitions, const int32_t* splits,
+                 const int32_t* block_table, const PartitionArgs& a) {
+  decltype(&wide_kernel<0, 16, false>) kernel;
+  if (kv8)
+    kernel = dtype == MLA_F16
+                 ? (block_size == 16 ? wide_kernel<0, 16, true> : wide_kernel<0, 32, true>)
+                 : (block_size == 16 ? wide_kernel<1, 16, true> : wide_kernel<1, 32, true>);
+  else
+    kernel = dtype == MLA_F16
+                 ? (block_size == 16 ? wide_kernel<0, 16, false> : wide_kernel<0, 32, false>)
+                 : (block_size == 16 ? wide_kernel<1, 16, false> : wide_kernel<1, 32, false>);
   hipLaunchKernelGGL(kernel, dim3(wgs), dim3(THREADS), 0, stream, groups, rows_per_req, slots,
                      flags, total_rows, max_blocks, context_lens, row_indptr, partitions, splits,
                      block_table, a);

@@ -218,7 +218,7 @@ def main():
                     help="tokens per cache block of the paged layout")
     ap.add_argument("--kv-fp8", action="store_true",
                     help="latent cache stored as E4M3 bytes times a scale of 2^-5 "
-                         "(mla_decode_partition_fp8; 16-head workgroups)")
+                         "(mla_decode_partition_fp8)")
     ap.add_argument("--fused", action="store_true",
                     help="partition and merge in one launch (mla_decode_fused)")
     ap.add_argument("--projections", action="store_true",
@@ -280,9 +280,6 @@ def main():
     table = torch.from_numpy(case.block_table).to(dev)
     ctx = torch.from_numpy(case.context_lens).to(dev)
     prm = mla.PlanParams(force_partitions=1, force_splits=1) if args.single_pass else None
-    if args.kv_fp8:
-        prm = prm or mla.PlanParams()
-        prm.heads_per_wg = 16
     plan = mla.DecodePlan(case.context_lens, case.heads, prm, device=dev, q_len=case.q_len,
                           block_size=case.block_size)
     qrows = case.q_len * case.heads

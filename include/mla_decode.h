@@ -255,8 +255,8 @@ int mla_decode_partition(const void* q_absorbed, const void* q_pe, const void* c
  * kpe_cache   dev uint8 [num_blocks, block_size, 64], 16-byte aligned
  * kv_scale    the cache scale (finite, > 0; MLA_E_RANGE otherwise)
  * dtype       the 16-bit type of q_absorbed, q_pe and out
- * heads_per_wg must be 16 (or 0, which means 16 here): plan with
- *             heads_per_wg = 16; MLA_E_UNSUPPORTED otherwise.
+ * heads_per_wg 16 or 64 (or 0: the default for num_heads), as for
+ *             mla_decode_partition; both workgroup shapes take E4M3 caches.
  * Errors: as mla_decode_partition.
  */
 int mla_decode_partition_fp8(const void* q_absorbed, const void* q_pe, const void* ckv_cache,

@@ -295,7 +295,7 @@ def test_decode_partition_fp8_host_checks_launch_nothing():
             a["maxb"], a["ctx"], a["batch"], a["heads"], a["qlen"], a["scale"], a["dtype"],
             a["P"], a["S"], a["ind"], a["rows"], a["maxr"], a["hpw"], a["po"], a["pl"],
             a["out"], a["lo"], a["dbg"], a["stream"])
-    assert call(hpw=64, heads=128) == -6      # E4M3 caches run 16-head workgroups
+    assert call(hpw=64, heads=48) == -6       # 64 does not divide 48 heads
     assert call(ks=0.0) == -3
     assert call(ks=-2.0) == -3
     assert call(ks=float("inf")) == -3

@@ -60,9 +60,11 @@ def test_graph_replays_equal_eager(name, fused, q_len):
 
 @pytest.mark.parametrize("name,block_size,fp8", [("v2lite_32k", 16, False), ("v3_81k", 16, False),
                                                  ("v2lite_32k", 32, True),
-                                                 ("two_req_32k_20k", 16, True)])
+                                                 ("two_req_32k_20k", 16, True),
+                                                 ("v3_81k", 32, True)])
 def test_graph_replays_equal_eager_cache_layouts(name, block_size, fp8):
-    # 16-token blocks and E4M3 byte caches, captured and replayed the same way.
+    # 16-token blocks and E4M3 byte caches (16- and 64-head workgroups),
+    # captured and replayed the same way.
     import torch
     kw = dict(kv_dtype="fp8_e4m3", kv_scale=2.0 ** -5) if fp8 else {}
     case = mla_synth.make_workload(name, block_size=block_size, **kw)
@@ -70,9 +72,7 @@ def test_graph_replays_equal_eager_cache_layouts(name, block_size, fp8):
     if fp8:
         dev["ckv_cache"] = torch.from_numpy(case.ckv_pool).cuda()
         dev["kpe_cache"] = torch.from_numpy(case.kpe_pool).cuda()
-    plan = mla.DecodePlan(case.context_lens, case.heads,
-                          mla.PlanParams(heads_per_wg=16) if fp8 else None,
-                          block_size=block_size)
+    plan = mla.DecodePlan(case.context_lens, case.heads, None, block_size=block_size)
     out = torch.empty((case.batch, case.heads, 512), dtype=torch_dtype(case.dtype), device="cuda")
     lse = torch.empty((case.batch, case.heads), dtype=torch.float32, device="cuda")
     stream = torch.cuda.Stream()

@@ -51,7 +51,9 @@ def draw_case(i):
     elif mode == 3:
         prm = dict(num_cus=int(rng.choice([64, 512, 2048])), min_tile_blocks=1)
     if fp8:
-        prm["heads_per_wg"] = 16
+        # E4M3 runs in both workgroup shapes: 64 heads where 64 divides the
+        # head count in every other case, else 16.
+        prm["heads_per_wg"] = 64 if heads % 64 == 0 and i % 2 == 0 else 16
     elif rng.random() < 0.3:
         prm["heads_per_wg"] = 16
     fused = (not fp8 and prm.get("heads_per_wg", 16 if heads % 64 else 64) == 16
