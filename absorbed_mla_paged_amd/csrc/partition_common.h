@@ -59,8 +59,17 @@ constexpr float RESCALE_LOG2 = 8.0f;    // lazy-rescale threshold (base 2)
 
 #ifdef __HIPCC__
 // XOR swizzles of the 16-byte chunk index inside an LDS row: ckv rows hold
-// 64 chunks (the low 4 bits are permuted), kpe rows 8.
-__device__ __forceinline__ int swz_ckv(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+// 64 chunks (the low 4 bits are permuted, by r % 16 only), kpe rows 8. Any
+// 16 consecutive ckv rows (a score read) take all 16 values, and
+// swz_ckv >> 1 is one-to-one on each of the row sets {0..7}, {8..15},
+// {0..3, 8..11} and {4..7, 12..15}: the transposing value reads (rows
+// 4 lg + ln / 4, two chunks of each) then fall in distinct banks whichever
+// two 16-lane groups the LDS serves together. (The bank-conflict counter
+// shows lane groups 0 and 2 served together: with rows r and r + 8 sharing
+// a chunk pair, every transposing read conflicted.)
+__device__ __forceinline__ int swz_ckv(int r) {
+  return (((r & 7) ^ ((r >> 1) & 4)) << 1) | ((r >> 3) & 1);
+}
 __device__ __forceinline__ int swz_kpe(int r) { return (r >> 1) & 7; }
 
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
