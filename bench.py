@@ -48,17 +48,17 @@ FETCH_SCALE = 2.0
 WRITE_SCALE = 1.0
 MEASURED = {
     # profiles/partition_kernel_v2lite_32k.md
-    ("v2lite_32k", "438a65f0bd2a"): dict(fetch_kib=18626.2, write_kib=8208.0, mfma_busy=0.022),
-    ("v2lite_32k@bs16", "438a65f0bd2a"): dict(fetch_kib=18627.7, write_kib=8208.0,
+    ("v2lite_32k", "62a2d525416b"): dict(fetch_kib=18631.7, write_kib=8208.0, mfma_busy=0.022),
+    ("v2lite_32k@bs16", "62a2d525416b"): dict(fetch_kib=18633.7, write_kib=8208.0,
                                               mfma_busy=0.022),
     # profiles/partition_kernel_v2lite_32k_fp8.md
-    ("v2lite_32k@fp8_e4m3", "438a65f0bd2a"): dict(fetch_kib=9424.5, write_kib=8208.0,
+    ("v2lite_32k@fp8_e4m3", "62a2d525416b"): dict(fetch_kib=9426.6, write_kib=8208.0,
                                                   mfma_busy=0.024),
     # profiles/wide_kernel_v3_131k.md
-    ("v3_131k", "157793657d21"): dict(fetch_kib=74491.8, write_kib=32832.0, mfma_busy=0.287),
+    ("v3_131k", "2ee7e513cb59"): dict(fetch_kib=74502.2, write_kib=32832.0, mfma_busy=0.285),
     # profiles/wide_kernel_v3_131k_fp8.md
-    ("v3_131k@fp8_e4m3", "157793657d21"): dict(fetch_kib=37626.8, write_kib=32832.0,
-                                               mfma_busy=0.279),
+    ("v3_131k@fp8_e4m3", "2ee7e513cb59"): dict(fetch_kib=37626.7, write_kib=32832.0,
+                                               mfma_busy=0.274),
 }
 
 
