@@ -56,6 +56,8 @@ MEASURED = {
                                                   mfma_busy=0.024),
     # profiles/wide_kernel_v3_131k.md
     ("v3_131k", "2ee7e513cb59"): dict(fetch_kib=74502.2, write_kib=32832.0, mfma_busy=0.285),
+    # profiles/wide_kernel_v3_81k.md
+    ("v3_81k", "2ee7e513cb59"): dict(fetch_kib=46882.6, write_kib=32062.5, mfma_busy=0.232),
     # profiles/wide_kernel_v3_131k_fp8.md
     ("v3_131k@fp8_e4m3", "2ee7e513cb59"): dict(fetch_kib=37626.7, write_kib=32832.0,
                                                mfma_busy=0.274),
