@@ -9,14 +9,17 @@
 // "How #898's merge kernel is reused"; zero weight for rows with no visible
 // key and a single rounding after the merge per MTPLX pull request 639.)
 //
-// One workgroup handles (b, h, a 32-dim slice): 32 row lanes x 8 threads,
-// each thread owning 4 consecutive dims (one 16-byte load per row), so a
-// row's slice is one 128-byte line. Row lane k takes rows k, k+32, ... in
-// order, with 8 rows' loads (slice and lse2) issued before any is used, so
-// a request's whole partial set is in flight at once, in a single round
-// trip. Each row lane keeps its own running maximum, weighted sum and
-// weight; the 32 row lanes are then merged in a fixed tree order (lane
-// shuffles, then the four waves), so the result is bit-identical run to run.
+// One workgroup handles (b, h, a slice of 32 or 64 dims): 256 threads as
+// row lanes x (slice / 4) threads, each thread owning 4 consecutive dims
+// (one 16-byte load per row), so a row's slice is one 128- or 256-byte
+// piece. Row lane k takes rows k, k + RL, ... in order, with 8 rows' loads
+// (slice and lse2) issued before any is used, so a request's whole partial
+// set is in flight at once, in a single round trip. Each row lane keeps its
+// own running maximum, weighted sum and weight; the row lanes are then
+// merged in a fixed tree order (lane shuffles, then the four waves), so the
+// result is bit-identical run to run. The launch takes 64-dim slices when
+// that still gives at least 1024 workgroups (many heads: fewer, wider
+// workgroups), else 32-dim ones (16 heads: more workgroups in flight).
 #include "device_common.h"
 #include "internal.h"
 
@@ -28,12 +31,9 @@ namespace {
 using namespace dev;
 
 constexpr int LAT = MLA_KV_LORA_RANK;
-constexpr int SLICE = 32;                 // dims per workgroup
-constexpr int SLICES = LAT / SLICE;       // 16
-constexpr int TPR = SLICE / 4;            // threads per row: 8
-constexpr int RL = 32;                    // row lanes
-constexpr int THREADS = TPR * RL;         // 256
+constexpr int THREADS = 256;
 constexpr int UNROLL = 8;                 // rows in flight per thread
+constexpr int WIDE_MIN_WGS = 1024;        // 64-dim slices from this many workgroups
 
 struct ReduceArgs {
   const float* partial_out;
@@ -46,8 +46,12 @@ struct ReduceArgs {
   int32_t total_rows;
 };
 
-template <int DT>
+template <int DT, int SLICE>
 __global__ __launch_bounds__(THREADS) void reduce_kernel(ReduceArgs a) {
+  constexpr int SLICES = LAT / SLICE;     // workgroups per (request, head)
+  constexpr int TPR = SLICE / 4;          // threads per row
+  constexpr int RL = THREADS / TPR;       // row lanes
+  static_assert(SLICE == 32 || SLICE == 64, "slice width");
   typedef Elem<DT> E;
   __shared__ f32x4 part[THREADS / 64][TPR];
   __shared__ float lane_m[THREADS / 64], lane_w[THREADS / 64];
@@ -106,8 +110,9 @@ __global__ __launch_bounds__(THREADS) void reduce_kernel(ReduceArgs a) {
       }
     }
   }
-  // Merge the row lanes: first the 8 of each wave through lane shuffles
-  // (lane bits 3..5), then the 4 waves through LDS, each in a fixed order.
+  // Merge the row lanes: first those of each wave through lane shuffles
+  // (the lane bits above the thread-in-row bits), then the 4 waves through
+  // LDS, each in a fixed order.
   auto merge = [&](float m2, float w2, f32x4 acc2) {
     const float mn = fmaxf(m, m2);
     const float s1 = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
@@ -117,7 +122,7 @@ __global__ __launch_bounds__(THREADS) void reduce_kernel(ReduceArgs a) {
     m = mn;
   };
 #pragma unroll
-  for (int x = 8; x < 64; x <<= 1) {
+  for (int x = TPR; x < 64; x <<= 1) {
     f32x4 acc2;
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc2[j] = shfl_xor(acc[j], x);
@@ -182,7 +187,8 @@ extern "C" int mla_decode_reduce(const float* partial_out, const float* partial_
       (partial_lse2 && !aligned(partial_lse2, 4)) || !aligned(row_indptr, 4) ||
       (lse2_out && !aligned(lse2_out, 4)))
     return fail(MLA_E_ALIGN, "misaligned buffer");
-  const int64_t wgs = (int64_t)batch * num_heads * SLICES;
+  const bool wide = (int64_t)batch * num_heads * (LAT / 64) >= WIDE_MIN_WGS;
+  const int64_t wgs = (int64_t)batch * num_heads * (LAT / (wide ? 64 : 32));
   if (wgs > INT32_MAX) return fail(MLA_E_SHAPE, "grid too large");
   ReduceArgs a;
   a.partial_out = partial_out;
@@ -193,10 +199,9 @@ extern "C" int mla_decode_reduce(const float* partial_out, const float* partial_
   a.batch = batch;
   a.heads = num_heads;
   a.total_rows = total_rows;
-  if (dtype == MLA_F16)
-    hipLaunchKernelGGL(reduce_kernel<0>, dim3((unsigned)wgs), dim3(THREADS), 0, stream, a);
-  else
-    hipLaunchKernelGGL(reduce_kernel<1>, dim3((unsigned)wgs), dim3(THREADS), 0, stream, a);
+  auto kernel = dtype == MLA_F16 ? (wide ? reduce_kernel<0, 64> : reduce_kernel<0, 32>)
+                                 : (wide ? reduce_kernel<1, 64> : reduce_kernel<1, 32>);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)wgs), dim3(THREADS), 0, stream, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(MLA_E_HIP, "reduce launch: %s", hipGetErrorString(e));
   count(2, 1);
