@@ -237,6 +237,38 @@ def test_reduce_all_empty_rows_give_zero():
     assert torch.all(out == 0) and torch.all(lse == float("-inf"))
 
 
+@pytest.mark.parametrize("batch,heads", [(1, 128), (2, 64), (8, 16), (1, 112), (4, 16)])
+def test_reduce_slice_widths(batch, heads):
+    # The reduce launch takes 64-dim slices when batch x heads x 8 reaches
+    # 1024 workgroups, else 32-dim ones: cases on both sides of that
+    # threshold (the first three at or above it), with random partials of
+    # uneven row counts, some rows empty (LSE -inf, zero partial) and a hot
+    # last row per request, against the oracle's merge.
+    import torch
+    rng = np.random.default_rng(140 + batch * heads)
+    rows = rng.integers(1, 200, size=batch)
+    rows[0] = 257
+    ind = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    total = int(ind[-1])
+    po = rng.standard_normal((total, heads, 512)).astype(np.float32)
+    pl = rng.uniform(-4.0, 12.0, size=(total, heads)).astype(np.float32)
+    empty = rng.random((total, heads)) < 0.1
+    pl[empty] = -np.inf
+    po[empty] = 0.0
+    pl[ind[1:] - 1] += 20.0
+    ref, lref = reference.merge_log2_f64(po, pl, ind)
+    out = torch.empty((batch, heads, 512), dtype=torch.float16, device="cuda")
+    lse = torch.empty((batch, heads), dtype=torch.float32, device="cuda")
+    mla.mla_decode_reduce(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda(),
+                          torch.from_numpy(ind).cuda(), batch, heads, total, out, lse)
+    torch.cuda.synchronize()
+    err = np.abs(out.float().cpu().numpy() - ref)
+    log(f"[reduce] B={batch} H={heads} rows={total}: max err {err.max():.3e} "
+        f"mean {err.mean():.3e}")
+    assert err.max() <= 1e-2 and err.mean() <= 1e-3
+    assert np.max(np.abs(lse.cpu().numpy() - lref)) < 1e-4
+
+
 # --- the path taken is provable ---------------------------------------------------
 
 def test_path_counters():
