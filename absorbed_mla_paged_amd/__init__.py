@@ -227,6 +227,91 @@ def _need_cuda(*ts):
             raise MlaError(-1, "device tensors are required (torch CUDA/HIP tensors)")
 
 
+# Argument checks made before any pointer crosses the ABI: the library sees
+# only pointers and sizes, so a tensor that is non-contiguous, of the wrong
+# element type or smaller than its declared shape would be read or written
+# out of bounds on the device. Every check raises MlaError: -2 (MLA_E_SHAPE)
+# for layout and shape, -6 (MLA_E_UNSUPPORTED) for element types.
+
+def _tensor(t, name, dtypes, shape=None, numel=None, optional=False, min_numel=None):
+    """Check one tensor: present (unless optional), contiguous, of one of
+    `dtypes` (torch dtypes), and of `shape` (None entries are free), of
+    `numel` elements, or of at least `min_numel`."""
+    if t is None:
+        if optional:
+            return
+        raise MlaError(-1, f"{name} is required")
+    if t.dtype not in dtypes:
+        raise MlaError(-6, f"{name}: dtype {t.dtype}, need {' or '.join(str(d) for d in dtypes)}")
+    if not t.is_contiguous():
+        raise MlaError(-2, f"{name} must be contiguous")
+    if shape is not None:
+        if t.dim() != len(shape) or any(w is not None and int(g) != int(w)
+                                        for g, w in zip(t.shape, shape)):
+            want = "[" + ", ".join("*" if w is None else str(w) for w in shape) + "]"
+            raise MlaError(-2, f"{name}: shape {list(t.shape)}, need {want}")
+    if numel is not None and t.numel() != int(numel):
+        raise MlaError(-2, f"{name}: {t.numel()} elements, need {int(numel)}")
+    if min_numel is not None and t.numel() < int(min_numel):
+        raise MlaError(-2, f"{name}: {t.numel()} elements, need at least {int(min_numel)}")
+
+
+def _same_device(*ts):
+    devs = {str(t.device) for t in ts if t is not None}
+    if len(devs) > 1:
+        raise MlaError(-2, f"tensors on different devices: {sorted(devs)}")
+
+
+def _f16_types():
+    import torch
+    return (torch.float16, torch.bfloat16)
+
+
+def _check_decode_args(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens,
+                       partitions, splits, row_indptr, total_rows, partial_out, partial_lse2,
+                       out, lse2_out, debug_ranges, q_len, cache_dtypes):
+    """Shapes and types of a partition launch; returns (B, H, Q)."""
+    import torch
+    f16 = _f16_types()
+    i32 = (torch.int32,)
+    f32 = (torch.float32,)
+    if q_absorbed is None:
+        raise MlaError(-1, "q_absorbed is required")
+    if q_absorbed.dim() not in (3, 4) or int(q_absorbed.shape[-1]) != KV_LORA_RANK:
+        raise MlaError(-2, f"q_absorbed: shape {list(q_absorbed.shape)}, need [B, Q*H, 512] "
+                           f"or [B, Q, H, 512]")
+    B, H, Q = _query_shape(q_absorbed, q_len)
+    if Q < 1 or (q_absorbed.dim() == 3 and int(q_absorbed.shape[1]) != Q * H):
+        raise MlaError(-2, f"q_absorbed: {int(q_absorbed.shape[1])} rows is not q_len "
+                           f"{Q} x heads")
+    _tensor(q_absorbed, "q_absorbed", f16)
+    qd = (q_absorbed.dtype,)
+    _tensor(q_pe, "q_pe", qd, numel=B * Q * H * ROPE_DIM)
+    if q_pe.shape[0] != B or int(q_pe.shape[-1]) != ROPE_DIM:
+        raise MlaError(-2, f"q_pe: shape {list(q_pe.shape)}, need [B, Q*H, 64] or [B, Q, H, 64]")
+    _tensor(ckv_cache, "ckv_cache", cache_dtypes, shape=(None, None, KV_LORA_RANK))
+    nb, bs = int(ckv_cache.shape[0]), int(ckv_cache.shape[1])
+    _tensor(kpe_cache, "kpe_cache", (ckv_cache.dtype,), shape=(nb, bs, ROPE_DIM))
+    _tensor(block_table, "block_table", i32, shape=(B, None))
+    _tensor(context_lens, "context_lens", i32, shape=(B,))
+    rows = int(total_rows)
+    split = rows != B
+    _tensor(partitions, "partitions", i32, shape=(B,), optional=not split)
+    _tensor(splits, "splits", i32, shape=(B,), optional=not split)
+    _tensor(row_indptr, "row_indptr", i32, shape=(B + 1,), optional=not split)
+    _tensor(partial_out, "partial_out", f32, shape=(rows, Q * H, KV_LORA_RANK),
+            optional=not split)
+    _tensor(partial_lse2, "partial_lse2", f32, shape=(rows, Q * H), optional=not split)
+    _tensor(out, "out", qd, numel=B * Q * H * KV_LORA_RANK, optional=split)
+    if out is not None and int(out.shape[0]) != B:
+        raise MlaError(-2, f"out: shape {list(out.shape)}, need [B, Q*H, 512]")
+    _tensor(lse2_out, "lse2_out", f32, numel=B * Q * H, optional=True)
+    _tensor(debug_ranges, "debug_ranges", i32, min_numel=2 * rows, optional=True)
+    _same_device(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens, partitions,
+                 splits, row_indptr, partial_out, partial_lse2, out, lse2_out, debug_ranges)
+    return B, H, Q
+
+
 def mla_decode_partition(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens,
                          scale: float, partitions, splits, row_indptr, total_rows: int,
                          max_rows_per_req: int, heads_per_wg: int, partial_out, partial_lse2,
@@ -236,8 +321,13 @@ def mla_decode_partition(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, co
     tokens per request. The cache block size is ckv_cache.shape[1] (16 or
     32), and must be the one the plan was chosen for."""
     lib = load_library()
+    B, H, Q = _check_decode_args(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table,
+                                 context_lens, partitions, splits, row_indptr, total_rows,
+                                 partial_out, partial_lse2, out, lse2_out, debug_ranges, q_len,
+                                 _f16_types())
+    if ckv_cache.dtype != q_absorbed.dtype:
+        raise MlaError(-6, f"ckv_cache dtype {ckv_cache.dtype} differs from q_absorbed's")
     _need_cuda(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens)
-    B, H, Q = _query_shape(q_absorbed, q_len)
     _check(lib.mla_decode_partition(
         _ptr(q_absorbed), _ptr(q_pe), _ptr(ckv_cache), _ptr(kpe_cache), int(ckv_cache.shape[0]),
         int(ckv_cache.shape[1]), _ptr(block_table), int(block_table.shape[1]), _ptr(context_lens), B, H, Q,
@@ -256,10 +346,11 @@ def mla_decode_partition_fp8(q_absorbed, q_pe, ckv_cache, kpe_cache, kv_scale: f
     include/mla_decode.h), with 16 or 64 heads per workgroup."""
     import torch
     lib = load_library()
+    B, H, Q = _check_decode_args(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table,
+                                 context_lens, partitions, splits, row_indptr, total_rows,
+                                 partial_out, partial_lse2, out, lse2_out, debug_ranges, q_len,
+                                 (torch.uint8,))
     _need_cuda(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens)
-    if ckv_cache.dtype != torch.uint8 or kpe_cache.dtype != torch.uint8:
-        raise MlaError(-6, "E4M3 caches are passed as uint8 tensors")
-    B, H, Q = _query_shape(q_absorbed, q_len)
     _check(lib.mla_decode_partition_fp8(
         _ptr(q_absorbed), _ptr(q_pe), _ptr(ckv_cache), _ptr(kpe_cache), float(kv_scale),
         int(ckv_cache.shape[0]), int(ckv_cache.shape[1]), _ptr(block_table),
@@ -274,9 +365,20 @@ def mla_decode_fused(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, contex
                      max_rows_per_req: int, heads_per_wg: int, partial_out, partial_lse2,
                      out, lse2_out, sync, debug_ranges=None, stream=None, q_len=None):
     """Partition and merge in one launch (see include/mla_decode.h)."""
+    import torch
     lib = load_library()
+    B, H, Q = _check_decode_args(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table,
+                                 context_lens, partitions, splits, row_indptr, total_rows,
+                                 partial_out, partial_lse2, None, lse2_out, debug_ranges, q_len,
+                                 _f16_types())
+    if ckv_cache.dtype != q_absorbed.dtype:
+        raise MlaError(-6, f"ckv_cache dtype {ckv_cache.dtype} differs from q_absorbed's")
+    _tensor(out, "out", (q_absorbed.dtype,), numel=B * Q * H * KV_LORA_RANK)
+    if int(total_rows) != B:
+        _tensor(sync, "sync", (torch.int64,),
+                numel=max(1, B) * FUSED_SYNC_BYTES_PER_REQUEST // 8)
+    _same_device(q_absorbed, out, sync)
     _need_cuda(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens, out)
-    B, H, Q = _query_shape(q_absorbed, q_len)
     _check(lib.mla_decode_fused(
         _ptr(q_absorbed), _ptr(q_pe), _ptr(ckv_cache), _ptr(kpe_cache), int(ckv_cache.shape[0]),
         int(ckv_cache.shape[1]), _ptr(block_table), int(block_table.shape[1]), _ptr(context_lens), B, H, Q,
@@ -286,10 +388,28 @@ def mla_decode_fused(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, contex
         _stream(stream)))
 
 
+def fused_sync_errors(sync) -> int:
+    """Waits that ran out in a fused hand-off buffer: the sum of word 4 of
+    every 64-byte record (see mla_decode_fused in include/mla_decode.h).
+    Non-zero means a merge piece was skipped and `out` is unspecified for
+    the requests concerned. Reads the buffer back, so it waits for the
+    launches that use it to finish."""
+    words = sync.detach().to("cpu").view(-1)
+    return int(words.view(-1, 8)[:, 4].sum().item())
+
+
 def mla_decode_reduce(partial_out, partial_lse2, row_indptr, batch: int, num_heads: int,
                       total_rows: int, out, lse2_out=None, stream=None):
     """Launch the LSE-weighted reduce (see include/mla_decode.h)."""
+    import torch
     lib = load_library()
+    rows, B, H = int(total_rows), int(batch), int(num_heads)
+    _tensor(partial_out, "partial_out", (torch.float32,), shape=(rows, H, KV_LORA_RANK))
+    _tensor(partial_lse2, "partial_lse2", (torch.float32,), shape=(rows, H))
+    _tensor(row_indptr, "row_indptr", (torch.int32,), shape=(B + 1,))
+    _tensor(out, "out", _f16_types(), numel=B * H * KV_LORA_RANK)
+    _tensor(lse2_out, "lse2_out", (torch.float32,), numel=B * H, optional=True)
+    _same_device(partial_out, partial_lse2, row_indptr, out, lse2_out)
     _need_cuda(partial_out, partial_lse2, row_indptr, out)
     _check(lib.mla_decode_reduce(_ptr(partial_out), _ptr(partial_lse2), _ptr(row_indptr),
                                  int(batch), int(num_heads), int(total_rows), _dtype_code(out),
@@ -298,9 +418,15 @@ def mla_decode_reduce(partial_out, partial_lse2, row_indptr, batch: int, num_hea
 
 def _head_product(name, x, w, y, stream):
     lib = load_library()
+    _tensor(w, "weights", _f16_types(), shape=(None, None, None))
+    heads, din, dout = (int(v) for v in w.shape)
+    _tensor(x, "input", (w.dtype,))
+    if x.dim() < 2 or int(x.shape[-1]) != din or int(x.shape[-2]) != heads:
+        raise MlaError(-2, f"input: shape {list(x.shape)}, need [..., {heads}, {din}]")
+    rows = x.numel() // (heads * din) if x.numel() else 0
+    _tensor(y, "output", (w.dtype,), numel=rows * heads * dout)
+    _same_device(x, w, y)
     _need_cuda(x, w, y)
-    heads = int(w.shape[0])
-    rows = x.numel() // (heads * int(w.shape[1])) if x.numel() else 0
     _check(getattr(lib, name)(_ptr(x), _ptr(w), _ptr(y), rows, heads, _dtype_code(x),
                               _stream(stream)))
 
@@ -352,9 +478,10 @@ class DecodePlan:
 
 def decode(plan: DecodePlan, q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens,
            scale: float, out, lse2_out=None, debug_ranges=None, stream=None, fused=False,
-           kv_scale: float | None = None):
+           kv_scale: float | None = None, check_fused: bool = False):
     """Partition launch, then the reduce launch when the plan needs one; with
-    fused=True, one launch that merges too. uint8 caches are E4M3 bytes
+    fused=True, one launch that merges too (check_fused=True then waits for
+    it and raises if a hand-off wait ran out). uint8 caches are E4M3 bytes
     times kv_scale (mla_decode_partition_fp8)."""
     if int(ckv_cache.shape[1]) != plan.block_size:
         raise MlaError(-2, f"cache blocks of {int(ckv_cache.shape[1])} tokens, plan chosen for "
@@ -380,6 +507,10 @@ def decode(plan: DecodePlan, q_absorbed, q_pe, ckv_cache, kpe_cache, block_table
                          plan.info["max_rows_per_req"], plan.info["heads_per_wg"],
                          plan.partial_out, plan.partial_lse2, out, lse2_out, plan.sync,
                          debug_ranges, stream, q_len=plan.q_len)
+        if check_fused and plan.info["needs_reduce"]:
+            missed = fused_sync_errors(plan.sync)
+            if missed:
+                raise MlaError(-7, f"{missed} fused hand-off waits ran out; out is unspecified")
         return
     mla_decode_partition(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens, scale,
                          plan.partitions, plan.splits, plan.row_indptr, plan.total_rows,

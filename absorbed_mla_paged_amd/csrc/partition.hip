@@ -680,7 +680,8 @@ int partition_launch(bool fused, bool kv8, float kv_scale, const void* q_absorbe
     return fail(MLA_E_RANGE, "kv_scale must be finite and > 0");
   if (!valid_block_size(block_size))
     return fail(MLA_E_UNSUPPORTED, "block_size %d (16 or 32 are supported)", block_size);
-  if (!std::isfinite(scale)) return fail(MLA_E_RANGE, "scale is not finite");
+  if (!(std::isfinite(scale) && scale > 0.0f))
+    return fail(MLA_E_RANGE, "scale must be finite and > 0");
   if (batch == 0) return MLA_OK;
   if (!q_absorbed || !q_pe || !ckv_cache || !kpe_cache || !block_table || !context_lens)
     return fail(MLA_E_NULL, "null input pointer");

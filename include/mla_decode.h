@@ -214,7 +214,8 @@ int mla_partition_range(int32_t ctx, int32_t block_size, int32_t P, int32_t S,
  * context_lens dev int32 [batch], 0 <= n_b <= block_size * max_blocks_per_seq
  *             (clamped into that range on the device). Rows of the last
  *             block at t >= n_b may hold anything, NaN included.
- * scale       softmax scale applied to both score halves (finite, > 0)
+ * scale       softmax scale applied to both score halves (finite, > 0; MLA_E_RANGE
+ *             otherwise)
  * partitions, splits dev int32 [batch]; row_indptr dev int32 [batch+1]:
  *             the chooser's arrays, copied to the device by the caller.
  * total_rows, max_rows_per_req: from mla_plan_info.
@@ -320,7 +321,12 @@ int mla_decode_reduce(const float* partial_out, const float* partial_lse2,
  *             same sync buffer must not run concurrently, and after a
  *             launch that did not complete it must be zero-filled again.
  *             Word 4 of each 64-byte record counts waits that ran out
- *             (0 in correct use).
+ *             (0 in correct use). A wait that runs out skips its share of
+ *             the merge, and the call still returns MLA_OK: `out` and
+ *             `lse2_out` are then unspecified for that request. Callers that
+ *             cannot rule this out (e.g. a sync buffer shared by concurrent
+ *             launches) read word 4 back after the launch completes (the
+ *             Python binding's fused_sync_errors does).
  * Currently heads_per_wg must be 16 for split plans, with at most 8 head
  * groups per request (q_len * num_heads <= 128); MLA_E_UNSUPPORTED
  * otherwise.

@@ -82,6 +82,28 @@ def latent_brute(case, b: int, h: int):
     return [x / den for x in num], mpmath.log(den) / mpmath.log(2)
 
 
+def weight_moments_brute(case, b: int, h: int):
+    """sum_t w_t and sum_t w_t^2 with w_t = exp(s_t - max_t s_t), by the
+    definition (scores by plain sums, the maximum found first)."""
+    n = int(case.context_lens[b])
+    bs = int(case.ckv_pool.shape[1])
+    qa = [_bits_to_mpf(v, case.dtype) for v in case.q_absorbed[b][h]]
+    qp = [_bits_to_mpf(v, case.dtype) for v in case.q_pe[b][h]]
+    scale = mpmath.mpf(case.scale)
+    scores = []
+    for t in range(n):
+        phys = int(case.block_table[b][t // bs])
+        c = _cache_row(case, case.ckv_pool, phys, t % bs)
+        k = _cache_row(case, case.kpe_pool, phys, t % bs)
+        scores.append(scale * (mpmath.fsum(x * y for x, y in zip(qa, c))
+                               + mpmath.fsum(x * y for x, y in zip(qp, k))))
+    if not scores:
+        return mpmath.mpf(0), mpmath.mpf(0)
+    top = max(scores)
+    w = [mpmath.exp(s - top) for s in scores]
+    return mpmath.fsum(w), mpmath.fsum(x * x for x in w)
+
+
 def latent_brute_window(case, b: int, j: int, h: int):
     """Head h of new token j in a window of case.q_len new tokens, by the
     definition with an explicit causal mask: token j sits at position

@@ -85,20 +85,25 @@ def _attend(qa, qp, C, Kp, scale):
     output sum_t w_t C_t / sum_t w_t; lse2 = (max + ln sum w) / ln 2.
     (mlxcel pull request 995, "What changed", Stage 1.)
     qa [h, 512], qp [h, 64] float64.
+
+    Also returns the first two moments of the weights, sum_t w_t and
+    sum_t w_t^2 (w_t = exp(s_t - max), so the largest weight is 1): they
+    say how many tokens carry the softmax, which sizes the rounding error a
+    GPU sum of 16-bit weights can have.
     """
     h = qa.shape[0]
     if C.shape[0] == 0:
         # No visible token: zero output, lse2 = -inf, so the row carries
         # weight 0 in any merge (MTPLX pull request 639, commit on rows
         # without a visible key).
-        return np.zeros((h, LATENT)), np.full(h, -np.inf)
+        return np.zeros((h, LATENT)), np.full(h, -np.inf), np.zeros(h), np.zeros(h)
     s = scale * (qa @ C.T + qp @ Kp.T)            # [h, k]
     m = s.max(axis=1, keepdims=True)
     w = np.exp(s - m)
     z = w.sum(axis=1)
     out = (w @ C) / z[:, None]
     lse2 = (m[:, 0] + np.log(z)) / LN_2
-    return out, lse2
+    return out, lse2, z, (w * w).sum(axis=1)
 
 
 def visible_len(n: int, q_len: int, j: int) -> int:
@@ -113,15 +118,19 @@ def visible_len(n: int, q_len: int, j: int) -> int:
     return max(0, n - q_len + 1 + j)
 
 
-def latent_one(case, b: int, heads=None, lo: int = 0, hi: int | None = None):
+def latent_one(case, b: int, heads=None, lo: int = 0, hi: int | None = None,
+               moments: bool = False):
     """Oracle output for request b (optionally a subset of query rows / a
-    token range). Query row j * H + h is head h of new token j."""
+    token range). Query row j * H + h is head h of new token j. With
+    moments=True also the weight moments sum w and sum w^2 of each row."""
     n = int(case.context_lens[b])
     q_len = int(getattr(case, "q_len", 1))
     rows = np.arange(q_len * case.heads) if heads is None else np.asarray(heads)
     hi = n if hi is None else hi
     out = np.zeros((rows.size, LATENT))
     lse2 = np.zeros(rows.size)
+    w1 = np.zeros(rows.size)
+    w2 = np.zeros(rows.size)
     for j in sorted(set((rows // case.heads).tolist())):
         sel = rows // case.heads == j
         C, Kp = gather_request(case.ckv_pool, case.kpe_pool, case.block_table[b], n,
@@ -129,25 +138,30 @@ def latent_one(case, b: int, heads=None, lo: int = 0, hi: int | None = None):
                                getattr(case, "kv_dtype", None), getattr(case, "kv_scale", 1.0))
         qa = decode16(case.q_absorbed[b, rows[sel]], case.dtype)
         qp = decode16(case.q_pe[b, rows[sel]], case.dtype)
-        out[sel], lse2[sel] = _attend(qa, qp, C, Kp, case.scale)
+        out[sel], lse2[sel], w1[sel], w2[sel] = _attend(qa, qp, C, Kp, case.scale)
+    if moments:
+        return out, lse2, w1, w2
     return out, lse2
 
 
-def latent_f64(case, requests=None, heads=None):
+def latent_f64(case, requests=None, heads=None, moments: bool = False):
     """Single-pass absorbed decode for a whole batch (or a sample of it).
 
     Returns out [B, q_len * H, 512] and lse2 [B, q_len * H]; entries outside
-    the requested sample are NaN.
+    the requested sample are NaN. With moments=True, also the weight moments
+    sum_t w_t and sum_t w_t^2 [B, q_len * H] (w_t = exp(s_t - max s)).
     """
     B, H = case.batch, int(getattr(case, "q_len", 1)) * case.heads
     out = np.full((B, H, LATENT), np.nan)
     lse2 = np.full((B, H), np.nan)
+    w1 = np.full((B, H), np.nan)
+    w2 = np.full((B, H), np.nan)
     reqs = range(B) if requests is None else requests
     hs = np.arange(H) if heads is None else np.asarray(heads)
     for b in reqs:
-        o, l = latent_one(case, b, hs)
-        out[b, hs] = o
-        lse2[b, hs] = l
+        out[b, hs], lse2[b, hs], w1[b, hs], w2[b, hs] = latent_one(case, b, hs, moments=True)
+    if moments:
+        return out, lse2, w1, w2
     return out, lse2
 
 

@@ -13,10 +13,37 @@ import oracle
 # Acceptance bounds on the latent output (fp16/bf16 inputs, fp32 accumulate).
 MAX_ABS = 1e-2
 MEAN_ABS = 1e-3
-# LSE bound derived from the arithmetic: the weights are rounded to the
-# 16-bit type before they are summed, a relative error of at most u per
-# weight, so |d log2 l| <= log2(e) * u; plus fp32 slack.
-LSE_TOL = {"f16": 1.4427 * 2.0 ** -11 + 2e-5, "bf16": 1.4427 * 2.0 ** -8 + 2e-5}
+# Relative L2 error of the whole output against the oracle's: bf16 output
+# rounding alone is about 2^-9 / sqrt(3); a dropped 32-token block at
+# 131072 tokens moves it past 1e-2.
+REL_L2 = 1e-2
+# Unit roundoff of the 16-bit types the weights are rounded to.
+UNIT = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+LOG2E = 1.4426950408889634
+# Worst-case LSE bound derived from the arithmetic: the weights are rounded
+# to the 16-bit type before they are summed, a relative error of at most u
+# per weight, so |d log2 l| <= log2(e) * u; plus fp32 slack.
+LSE_SLACK = 2e-5
+LSE_TOL = {k: LOG2E * u + LSE_SLACK for k, u in UNIT.items()}
+
+
+def lse_bound(dtype: str, w1=None, w2=None):
+    """Per-row LSE bound. With the oracle's weight moments (w1 = sum w,
+    w2 = sum w^2, w = exp(s - max s)): the rounding errors of the weights
+    are independent, each uniform within +-u relative, so the error of
+    log(sum w) has standard deviation (u / sqrt 3) * sqrt(w2) / w1; six of
+    those, never more than the worst case log2(e) * u, plus fp32 slack. At
+    131072 near-uniform weights this is ~8e-5 for bf16, below the 3.5e-4 a
+    dropped 32-token block moves the LSE by."""
+    u = UNIT[dtype]
+    if w1 is None:
+        return LSE_TOL[dtype]
+    w1 = np.asarray(w1, dtype=np.float64)
+    w2 = np.asarray(w2, dtype=np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        stat = LOG2E * 6.0 * (u / math.sqrt(3.0)) * np.sqrt(w2) / w1
+    stat = np.where(np.isfinite(stat), stat, LOG2E * u)
+    return np.minimum(stat, LOG2E * u) + LSE_SLACK
 
 
 def log(msg: str):
@@ -65,26 +92,60 @@ def run_case(case, params: mla.PlanParams | None = None, dev=None, want_ranges=F
     return o, l, plan, r
 
 
-def compare(case, out, lse2, ref, lref, what=""):
-    """Assert the acceptance bounds; return the error summary."""
+def compare(case, out, lse2, ref, lref, what="", moments=None):
+    """Assert the acceptance bounds; return the error summary. `moments` is
+    (w1, w2) from oracle.latent_f64(..., moments=True): with it the LSE bound
+    shrinks with the number of tokens that carry the softmax (lse_bound)."""
     sel = ~np.isnan(lref)
     d = np.abs(out - ref)[sel]
     finite = np.isfinite(lref) & sel
     dl = np.abs(lse2[finite] - lref[finite])
+    if moments is not None:
+        tol = lse_bound(case.dtype, moments[0][finite], moments[1][finite])
+    else:
+        tol = np.full(dl.shape, LSE_TOL[case.dtype])
     rel = float(np.linalg.norm(d) / max(1e-30, np.linalg.norm(ref[sel])))
     summary = dict(max_abs=float(d.max()) if d.size else 0.0,
                    mean_abs=float(d.mean()) if d.size else 0.0,
-                   rel_l2=rel, lse_max=float(dl.max()) if dl.size else 0.0)
+                   rel_l2=rel, lse_max=float(dl.max()) if dl.size else 0.0,
+                   lse_over_bound=float((dl / tol).max()) if dl.size else 0.0)
     log(f"[parity] {what} {summary}")
-    assert np.all(np.isfinite(out)), f"{what}: non-finite output"
+    assert np.all(np.isfinite(out[sel])), f"{what}: non-finite output"
     assert summary["max_abs"] <= MAX_ABS, (what, summary)
     assert summary["mean_abs"] <= MEAN_ABS, (what, summary)
-    assert summary["lse_max"] <= LSE_TOL[case.dtype], (what, summary)
+    assert summary["rel_l2"] <= REL_L2, (what, summary)
+    assert np.all(dl <= tol), (what, summary)
     # Requests with nothing visible: zeros and -inf exactly.
     for b in range(case.batch):
         if int(case.context_lens[b]) == 0:
             assert np.all(out[b] == 0) and np.all(lse2[b] == -np.inf)
     return summary
+
+
+def half_ulp(x, dtype):
+    """Half a unit in the last place of |x| in the 16-bit output type
+    (normal range; fp16 subnormals and bf16 values below 2^-126 share the
+    smallest normal's spacing)."""
+    mant = 10 if dtype == "f16" else 7
+    emin = -14 if dtype == "f16" else -126
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** emin)))
+    return 0.5 * 2.0 ** (e - mant)
+
+
+def compare_beyond_rounding(case, out, lse2, ref, lref, what):
+    """Bounds for outputs that dominant tokens (needles with +-6 latent
+    values) push far past N(0,1) size: rounding such an output to the
+    16-bit type alone costs up to half an ulp (1.6e-2 at 6 in bf16), more
+    than the 1e-2 meant for N(0,1)-sized outputs. The error beyond that
+    rounding is held to the same thresholds."""
+    sel = ~np.isnan(lref)
+    excess = np.maximum(0.0, np.abs(out - ref) - half_ulp(ref, case.dtype))[sel]
+    log(f"[parity] {what} excess max {excess.max():.3e} mean {excess.mean():.3e} "
+        f"raw max {np.abs(out - ref)[sel].max():.3e}")
+    assert np.all(np.isfinite(out)), what
+    assert excess.max() <= 1e-2 and excess.mean() <= 1e-3, what
+    finite = np.isfinite(lref) & sel
+    assert np.max(np.abs(lse2 - lref)[finite]) <= LSE_TOL[case.dtype], what
 
 
 def sync_records(plan):

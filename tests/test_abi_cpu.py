@@ -209,6 +209,8 @@ def test_decode_partition_host_checks_launch_nothing():
     assert call(heads=128, hpw=128) == -6   # no 128-head layout
     assert call(heads=96, hpw=64) == -6     # 64 must divide H
     assert call(scale=float("nan")) == -3
+    assert call(scale=0.0) == -3          # the scale must be > 0: the 64-head kernel
+    assert call(scale=-0.07) == -3        # tracks unscaled maxima
     assert call(qa=None) == -1
     assert call(po=None) == -1          # split plan without workspace
     assert call(rows=1, out=None) == -1  # single pass without out

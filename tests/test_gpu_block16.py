@@ -33,8 +33,8 @@ def check(case, prm, fused=False, what=""):
     out, lse2, plan, ranges = run_case(case, mla.PlanParams(**prm), want_ranges=True, fused=fused)
     log(f"[plan] {what} P={plan.info['P']} S={plan.info['S']} rows={plan.total_rows} "
         f"hpw={plan.info['heads_per_wg']} tile={plan.info['tile_blocks']}")
-    ref, lref = oracle.latent_f64(case)
-    compare(case, out, lse2, ref, lref, what)
+    ref, lref, *mom = oracle.latent_f64(case, moments=True)
+    compare(case, out, lse2, ref, lref, what, moments=mom)
     if plan.total_rows > case.batch:
         want = rows_of_plan(case, plan)
         got = [tuple(r) for r in ranges[:plan.total_rows]]

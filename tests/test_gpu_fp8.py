@@ -57,8 +57,8 @@ def check(case, prm, what):
     assert case.ckv_pool.dtype == np.uint8
     out, lse2, plan, ranges = run_fp8(case, prm)
     log(f"[plan] {what} P={plan.info['P']} S={plan.info['S']} rows={plan.total_rows}")
-    ref, lref = oracle.latent_f64(case)
-    compare(case, out, lse2, ref, lref, what)
+    ref, lref, *mom = oracle.latent_f64(case, moments=True)
+    compare(case, out, lse2, ref, lref, what, moments=mom)
     if plan.total_rows > case.batch:
         want = rows_of_plan(case, plan)
         got = [tuple(r) for r in ranges[:plan.total_rows]]

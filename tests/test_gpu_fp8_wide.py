@@ -54,8 +54,8 @@ def run_wide(case, prm):
 def check(case, prm, what):
     out, lse2, plan, ranges = run_wide(case, prm)
     log(f"[plan] {what} P={plan.info['P']} S={plan.info['S']} rows={plan.total_rows}")
-    ref, lref = oracle.latent_f64(case)
-    compare(case, out, lse2, ref, lref, what)
+    ref, lref, *mom = oracle.latent_f64(case, moments=True)
+    compare(case, out, lse2, ref, lref, what, moments=mom)
     if plan.total_rows > case.batch:
         want = rows_of_plan(case, plan)
         got = [tuple(r) for r in ranges[:plan.total_rows]]

@@ -46,8 +46,8 @@ def test_fused_workload_parity(name, prm):
     case = mla_synth.make_workload(name, poison=True)
     out, lse2, plan, ranges = run_case(case, mla.PlanParams(**prm), want_ranges=True, fused=True)
     log(f"[plan] P={plan.info['P']} S={plan.info['S']} rows={plan.total_rows}")
-    ref, lref = oracle.latent_f64(case)
-    compare(case, out, lse2, ref, lref, f"fused {name} {prm}")
+    ref, lref, *mom = oracle.latent_f64(case, moments=True)
+    compare(case, out, lse2, ref, lref, f"fused {name} {prm}", moments=mom)
     want = rows_of_plan(case, plan)
     got = [tuple(r) for r in ranges[:plan.total_rows]]
     assert got == [(lo, hi) for _, lo, hi in want]
@@ -73,8 +73,8 @@ def test_fused_edge_cases(contexts, heads, dtype, prm):
     case = small(700 + sum(contexts) % 89, contexts, heads, dtype, poison=True)
     out, lse2, plan, ranges = run_case(case, mla.PlanParams(**prm), want_ranges=True, fused=True)
     log(f"[plan] P={plan.info['P']} S={plan.info['S']} rows={plan.total_rows}")
-    ref, lref = oracle.latent_f64(case)
-    compare(case, out, lse2, ref, lref, f"fused edge {contexts} H={heads} {prm}")
+    ref, lref, *mom = oracle.latent_f64(case, moments=True)
+    compare(case, out, lse2, ref, lref, f"fused edge {contexts} H={heads} {prm}", moments=mom)
     want = rows_of_plan(case, plan)
     got = [tuple(r) for r in ranges[:plan.total_rows]]
     assert got == [(lo, hi) for _, lo, hi in want]
@@ -125,7 +125,7 @@ def test_fused_sync_buffer_reused_across_plans():
     import torch
     case = small(83, [9000, 2500], 16, "f16", poison=True)
     dev = to_device(case)
-    ref, lref = oracle.latent_f64(case)
+    ref, lref, *mom = oracle.latent_f64(case, moments=True)
     plans = [mla.DecodePlan(case.context_lens, 16, mla.PlanParams(**p)) for p in
              (dict(force_partitions=2, force_splits=7), dict(force_partitions=5),
               dict(force_partitions=2, force_splits=7))]
@@ -138,7 +138,8 @@ def test_fused_sync_buffer_reused_across_plans():
                    dev["block_table"], dev["context_lens"], case.scale, out, lse2, fused=True)
         torch.cuda.synchronize()
         compare(case, out.float().cpu().numpy().astype(np.float64),
-                lse2.cpu().numpy().astype(np.float64), ref, lref, f"plan {i} rows {plan.total_rows}")
+                lse2.cpu().numpy().astype(np.float64), ref, lref, f"plan {i} rows {plan.total_rows}",
+                moments=mom)
         check_sync_quiet(plan, f"plan {i}")
 
 

@@ -30,8 +30,8 @@ def check(case, prm, fused=False, what=""):
     out, lse2, plan, ranges = run_case(case, mla.PlanParams(**prm), want_ranges=True, fused=fused)
     log(f"[plan] {what} q_len={case.q_len} P={plan.info['P']} S={plan.info['S']} "
         f"rows={plan.total_rows} groups={plan.info['groups']}")
-    ref, lref = oracle.latent_f64(case)
-    compare(case, out, lse2, ref, lref, what)
+    ref, lref, *mom = oracle.latent_f64(case, moments=True)
+    compare(case, out, lse2, ref, lref, what, moments=mom)
     if plan.info["needs_reduce"] or plan.total_rows > case.batch:
         want = rows_of_plan(case, plan)
         got = [tuple(r) for r in ranges[:plan.total_rows]]

@@ -56,8 +56,8 @@ def test_workload_parity(name, prm):
     if name == "mixed_b8":
         assert all(1 <= p <= 8 for p in plan.info["P"])
         assert plan.info["partial_out_bytes"] + plan.info["partial_lse_bytes"] <= 64 << 20
-    ref, lref = oracle.latent_f64(case)
-    compare(case, out, lse2, ref, lref, f"{name} {prm}")
+    ref, lref, *mom = oracle.latent_f64(case, moments=True)
+    compare(case, out, lse2, ref, lref, f"{name} {prm}", moments=mom)
     want = rows_of_plan(case, plan)
     got = [tuple(r) for r in ranges[:plan.total_rows]]
     assert got == [(lo, hi) for _, lo, hi in want]
@@ -85,8 +85,8 @@ def test_edge_cases(contexts, heads, dtype, prm):
     log(f"[case] edge {contexts} H={heads} {dtype} {prm}")
     case = small(500 + sum(contexts) % 97, contexts, heads, dtype, poison=True)
     out, lse2, plan, ranges = run_case(case, mla.PlanParams(**prm), want_ranges=True)
-    ref, lref = oracle.latent_f64(case)
-    compare(case, out, lse2, ref, lref, f"edge {contexts} H={heads} {prm}")
+    ref, lref, *mom = oracle.latent_f64(case, moments=True)
+    compare(case, out, lse2, ref, lref, f"edge {contexts} H={heads} {prm}", moments=mom)
     want = rows_of_plan(case, plan)
     if plan.total_rows > len(contexts) or any(p * s > 1 for p, s in zip(plan.info["P"], plan.info["S"])):
         got = [tuple(r) for r in ranges[:plan.total_rows]]
@@ -166,7 +166,7 @@ def test_reduce_matches_oracle_merge_and_rejects_ln_lse():
     blocks = case.block_table[0, :8]
     hot = reference.decode16(case.ckv_pool[blocks], case.dtype) * 1.5
     case.ckv_pool[blocks] = mla_synth.encode16(hot.astype(np.float32), case.dtype)
-    ref, lref = oracle.latent_f64(case)
+    ref, lref, *mom = oracle.latent_f64(case, moments=True)
     ranges = oracle.row_ranges(case.context_lens, [4], [1])
     po, pl = oracle.partials_f64(case, ranges, [0, 4])
     ind = torch.tensor([0, 4], dtype=torch.int32, device="cuda")

@@ -78,8 +78,8 @@ def test_random_configuration(i):
         dev["kv_scale"] = case.kv_scale
     out, lse2, plan, ranges = run_case(case, mla.PlanParams(**prm), dev=dev, want_ranges=True,
                                        fused=fused)
-    ref, lref = oracle.latent_f64(case)
-    compare(case, out, lse2, ref, lref, what)
+    ref, lref, *mom = oracle.latent_f64(case, moments=True)
+    compare(case, out, lse2, ref, lref, what, moments=mom)
     if plan.total_rows > case.batch:
         want = rows_of_plan(case, plan)
         got = [tuple(r) for r in ranges[:plan.total_rows]]

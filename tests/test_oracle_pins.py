@@ -84,7 +84,7 @@ def test_absorption_identity(contexts, heads):
     for b in range(case.batch):
         C, Kp = oracle.gather_request(case.ckv_pool, case.kpe_pool, case.block_table[b],
                                       int(case.context_lens[b]), case.dtype)
-        o_lat, l_lat = reference._attend(qa[b], qp[b], C, Kp, case.scale)
+        o_lat, l_lat = reference._attend(qa[b], qp[b], C, Kp, case.scale)[:2]
         o_back = oracle.unabsorb_output(o_lat[None], W_UV_T)[0]
         assert np.max(np.abs(o_back - o_dec[b])) < 1e-12
         assert np.max(np.abs(l_lat - l_dec[b])) < 1e-12
@@ -148,6 +148,35 @@ def test_empty_context():
     out, lse2 = oracle.latent_f64(case)
     assert np.all(out[0] == 0) and np.all(lse2[0] == -np.inf)
     assert np.all(np.isfinite(out[1])) and np.all(np.isfinite(lse2[1]))
+
+
+# --- weight moments (they size the GPU acceptance's LSE bound) ----------------
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("contexts", [[1], [33], [70, 5]])
+def test_weight_moments_match_brute_force(dtype, contexts):
+    # sum_t w_t and sum_t w_t^2 with w_t = exp(s_t - max s), by 50-digit
+    # scalar loops that find the maximum first.
+    case = small_case(41 + contexts[0], contexts, dtype=dtype, poison=True)
+    _, _, w1, w2 = oracle.latent_f64(case, moments=True)
+    for b in range(case.batch):
+        for h in range(case.heads):
+            b1, b2 = brute.weight_moments_brute(case, b, h)
+            assert abs(w1[b, h] - float(b1)) <= 1e-12 * float(b1)
+            assert abs(w2[b, h] - float(b2)) <= 1e-12 * float(b2)
+            assert 1.0 <= w2[b, h] <= w1[b, h] <= contexts[b]
+
+
+def test_weight_moments_closed_forms():
+    # q = 0: every weight is 1, so both moments equal n; one token: both 1;
+    # no token: both 0.
+    case = small_case(45, [100, 1, 0], heads=2, dtype="bf16", poison=True)
+    case.q_absorbed[0] = 0
+    case.q_pe[0] = 0
+    _, _, w1, w2 = oracle.latent_f64(case, moments=True)
+    assert np.all(w1[0] == 100) and np.all(w2[0] == 100)
+    assert np.all(w1[1] == 1) and np.all(w2[1] == 1)
+    assert np.all(w1[2] == 0) and np.all(w2[2] == 0)
 
 
 # --- P3: needles ----------------------------------------------------------
@@ -326,8 +355,8 @@ def _mutant_attend_no_rope(qa, qp, C, Kp, scale):
 
 
 def _mutant_attend_ln_lse(qa, qp, C, Kp, scale):
-    o, l = ORIG_ATTEND(qa, qp, C, Kp, scale)
-    return o, l * reference.LN_2
+    o, l, w1, w2 = ORIG_ATTEND(qa, qp, C, Kp, scale)
+    return o, l * reference.LN_2, w1, w2
 
 
 def _mutant_attend_scale_twice(qa, qp, C, Kp, scale):
