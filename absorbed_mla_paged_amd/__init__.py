@@ -369,7 +369,7 @@ def mla_decode_fused(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, contex
     lib = load_library()
     B, H, Q = _check_decode_args(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table,
                                  context_lens, partitions, splits, row_indptr, total_rows,
-                                 partial_out, partial_lse2, None, lse2_out, debug_ranges, q_len,
+                                 partial_out, partial_lse2, out, lse2_out, debug_ranges, q_len,
                                  _f16_types())
     if ckv_cache.dtype != q_absorbed.dtype:
         raise MlaError(-6, f"ckv_cache dtype {ckv_cache.dtype} differs from q_absorbed's")

@@ -171,3 +171,14 @@ def test_fused_sync_buffer_is_checked():
     assert status_of(args, lambda a: mla.mla_decode_fused(**a)) == -2
     args["sync"] = torch.zeros(B * 64, dtype=torch.int64)
     assert status_of(args, lambda a: mla.mla_decode_fused(**a)) == -1
+
+
+def test_fused_single_pass_needs_no_workspace():
+    args = valid()
+    args.update(total_rows=B, max_rows_per_req=1, partitions=None, splits=None,
+                row_indptr=None, partial_out=None, partial_lse2=None, sync=None,
+                debug_ranges=None)
+    assert status_of(args, lambda a: mla.mla_decode_fused(**a)) == -1
+    args["out"] = None
+    assert status_of(args, lambda a: mla.mla_decode_fused(**a)) == -1 and \
+        "out" in str(pytest.raises(mla.MlaError, mla.mla_decode_fused, **args).value)
