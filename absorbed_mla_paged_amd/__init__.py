@@ -20,6 +20,7 @@ MLA_F16, MLA_BF16 = 0, 1
 KV_LORA_RANK, ROPE_DIM, BLOCK_SIZE = 512, 64, 32
 BLOCK_SIZES = (16, 32)   # cache block sizes the kernels are built for
 FUSED_SYNC_BYTES_PER_REQUEST = 512
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MLA_NOALLOC_SCRATCH_BYTES
 STATUS = {0: "MLA_OK", -1: "MLA_E_NULL", -2: "MLA_E_SHAPE", -3: "MLA_E_RANGE",
           -4: "MLA_E_ALIGN", -5: "MLA_E_WORKSPACE", -6: "MLA_E_UNSUPPORTED",
           -7: "MLA_E_HIP"}
@@ -27,7 +28,8 @@ STATUS = {0: "MLA_OK", -1: "MLA_E_NULL", -2: "MLA_E_SHAPE", -3: "MLA_E_RANGE",
 # Every function include/mla_decode.h declares.
 EXPORTS = ["mla_default_plan_params", "mla_choose_partitions", "mla_partition_range",
            "mla_decode_partition", "mla_decode_partition_fp8", "mla_decode_reduce",
-           "mla_decode_fused", "mla_absorb_query",
+           "mla_decode_fused", "mla_decode_noalloc", "mla_noalloc_scratch_bytes",
+           "mla_absorb_query",
            "mla_unabsorb_output", "mla_status_string",
            "mla_last_error", "mla_get_counters", "mla_reset_counters"]
 
@@ -93,6 +95,12 @@ def load_library(path: str | None = None):
                                      ctypes.c_float, i32, vp, vp, vp, i32, i32, i32,
                                      vp, vp, vp, vp, vp, vp, vp]
     lib.mla_decode_fused.restype = ctypes.c_int
+    lib.mla_decode_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, vp, i32, i32, i32,
+                                       ctypes.c_float, i32, vp, vp, vp, i32, i32, i32, vp, vp,
+                                       vp]
+    lib.mla_decode_noalloc.restype = ctypes.c_int
+    lib.mla_noalloc_scratch_bytes.argtypes = [i32, i32, i32]
+    lib.mla_noalloc_scratch_bytes.restype = ctypes.c_size_t
     for name in ("mla_absorb_query", "mla_unabsorb_output"):
         getattr(lib, name).argtypes = [vp, vp, vp, i32, i32, i32, vp]
         getattr(lib, name).restype = ctypes.c_int
@@ -269,8 +277,10 @@ def _f16_types():
 
 def _check_decode_args(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens,
                        partitions, splits, row_indptr, total_rows, partial_out, partial_lse2,
-                       out, lse2_out, debug_ranges, q_len, cache_dtypes):
-    """Shapes and types of a partition launch; returns (B, H, Q)."""
+                       out, lse2_out, debug_ranges, q_len, cache_dtypes,
+                       caller_workspace=True):
+    """Shapes and types of a partition launch; returns (B, H, Q). Without
+    caller workspace (the library's own scratch) `out` is always needed."""
     import torch
     f16 = _f16_types()
     i32 = (torch.int32,)
@@ -299,10 +309,12 @@ def _check_decode_args(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, cont
     _tensor(partitions, "partitions", i32, shape=(B,), optional=not split)
     _tensor(splits, "splits", i32, shape=(B,), optional=not split)
     _tensor(row_indptr, "row_indptr", i32, shape=(B + 1,), optional=not split)
-    _tensor(partial_out, "partial_out", f32, shape=(rows, Q * H, KV_LORA_RANK),
-            optional=not split)
-    _tensor(partial_lse2, "partial_lse2", f32, shape=(rows, Q * H), optional=not split)
-    _tensor(out, "out", qd, numel=B * Q * H * KV_LORA_RANK, optional=split)
+    if caller_workspace:
+        _tensor(partial_out, "partial_out", f32, shape=(rows, Q * H, KV_LORA_RANK),
+                optional=not split)
+        _tensor(partial_lse2, "partial_lse2", f32, shape=(rows, Q * H), optional=not split)
+    _tensor(out, "out", qd, numel=B * Q * H * KV_LORA_RANK,
+            optional=split and caller_workspace)
     if out is not None and int(out.shape[0]) != B:
         raise MlaError(-2, f"out: shape {list(out.shape)}, need [B, Q*H, 512]")
     _tensor(lse2_out, "lse2_out", f32, numel=B * Q * H, optional=True)
@@ -386,6 +398,35 @@ def mla_decode_fused(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, contex
         int(total_rows), int(max_rows_per_req), int(heads_per_wg), _ptr(partial_out),
         _ptr(partial_lse2), _ptr(out), _ptr(lse2_out), _ptr(sync), _ptr(debug_ranges),
         _stream(stream)))
+
+
+def mla_noalloc_scratch_bytes(total_rows: int, num_heads: int, q_len: int = 1) -> int:
+    """Scratch bytes mla_decode_noalloc needs for a plan (see the header)."""
+    return int(load_library().mla_noalloc_scratch_bytes(int(total_rows), int(num_heads),
+                                                        int(q_len)))
+
+
+def mla_decode_noalloc(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens,
+                       scale: float, partitions, splits, row_indptr, total_rows: int,
+                       max_rows_per_req: int, heads_per_wg: int, out, lse2_out=None,
+                       stream=None, q_len=None):
+    """The split decode with its partials in the library's fixed device
+    scratch instead of caller memory (see include/mla_decode.h): nothing is
+    allocated. Calls that overlap on one GPU race."""
+    lib = load_library()
+    B, H, Q = _check_decode_args(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table,
+                                 context_lens, partitions, splits, row_indptr, total_rows,
+                                 None, None, out, lse2_out, None, q_len, _f16_types(),
+                                 caller_workspace=False)
+    if ckv_cache.dtype != q_absorbed.dtype:
+        raise MlaError(-6, f"ckv_cache dtype {ckv_cache.dtype} differs from q_absorbed's")
+    _need_cuda(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, context_lens, out)
+    _check(lib.mla_decode_noalloc(
+        _ptr(q_absorbed), _ptr(q_pe), _ptr(ckv_cache), _ptr(kpe_cache), int(ckv_cache.shape[0]),
+        int(ckv_cache.shape[1]), _ptr(block_table), int(block_table.shape[1]), _ptr(context_lens),
+        B, H, Q, float(scale), _dtype_code(q_absorbed), _ptr(partitions), _ptr(splits),
+        _ptr(row_indptr), int(total_rows), int(max_rows_per_req), int(heads_per_wg), _ptr(out),
+        _ptr(lse2_out), _stream(stream)))
 
 
 def fused_sync_errors(sync) -> int:

@@ -369,6 +369,47 @@ int mla_absorb_query(const void* q_nope, const void* w_uk, void* q_absorbed, int
 int mla_unabsorb_output(const void* out_latent, const void* w_uv_t, void* o, int32_t rows,
                         int32_t num_heads, int32_t dtype, hipStream_t stream);
 
+/*
+ * mla_decode_noalloc -- the split decode without caller workspace.
+ *
+ * For callers that cannot allocate device memory between calls: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same result as mla_decode_partition followed by mla_decode_reduce
+ * (bit for bit, same plan), but the fp32 partials and their LSEs go to a
+ * fixed array inside this library's code object: MLA_NOALLOC_SCRATCH_BYTES
+ * on each GPU the library runs on, held until the process ends. Its device
+ * address is looked up once per device (hipGetSymbolAddress, with that
+ * device current). The call allocates and frees nothing.
+ *
+ * Every call on one GPU shares that GPU's array and leaves the last call's
+ * partials in it: calls that overlap on one GPU (different streams or
+ * threads) race and give unspecified results; serialise them. Nothing in
+ * the array needs clearing: every row of the plan is written before the
+ * reduce reads it.
+ *
+ * Arguments as mla_decode_partition, without partial_out, partial_lse2 and
+ * debug_ranges; out (always) and lse2_out (or NULL) as for
+ * mla_decode_reduce. A single-pass plan (total_rows == batch) needs no
+ * scratch and writes `out` directly.
+ * Errors: as mla_decode_partition; MLA_E_WORKSPACE when the plan's partials
+ * (mla_noalloc_scratch_bytes) exceed MLA_NOALLOC_SCRATCH_BYTES -- choose the
+ * plan with workspace_limit_bytes at most that size.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int mla_decode_noalloc(const void* q_absorbed, const void* q_pe, const void* ckv_cache,
+                       const void* kpe_cache, int32_t num_blocks, int32_t block_size,
+                       const int32_t* block_table, int32_t max_blocks_per_seq,
+                       const int32_t* context_lens, int32_t batch, int32_t num_heads,
+                       int32_t q_len, float scale, int32_t dtype, const int32_t* partitions,
+                       const int32_t* splits, const int32_t* row_indptr, int32_t total_rows,
+                       int32_t max_rows_per_req, int32_t heads_per_wg, void* out,
+                       float* lse2_out, hipStream_t stream);
+
+/* Scratch bytes mla_decode_noalloc uses for a plan: the partials
+ * [total_rows, q_len * num_heads, 512] fp32 (rounded up to 256 bytes) plus
+ * their LSEs (0 for negative arguments). */
+size_t mla_noalloc_scratch_bytes(int32_t total_rows, int32_t num_heads, int32_t q_len);
+
 /* Text for a status code (static storage). */
 const char* mla_status_string(int status);
 

@@ -276,6 +276,30 @@ def test_decode_reduce_host_checks():
     assert lib.mla_decode_reduce(g, g, g, 0, 16, 0, 0, g, None, None) == 0
 
 
+def test_decode_noalloc_host_checks_launch_nothing():
+    # Plans whose partials exceed the fixed scratch, and a missing or
+    # misaligned `out`, are refused before any HIP call.
+    lib = mla.load_library()
+    vp = ctypes.c_void_p
+    g = vp(0x10000)
+
+    def call(rows=2, out=g, batch=1, heads=128, lo=None):
+        return lib.mla_decode_noalloc(g, g, g, g, 4, 32, g, 4, g, batch, heads, 1, 0.07, 1, g, g,
+                                      g, rows, max(1, rows), 0, out, lo, None)
+    limit = mla.NOALLOC_SCRATCH_BYTES
+    assert mla.mla_noalloc_scratch_bytes(2, 128) == 2 * 128 * 513 * 4
+    rows_fit = limit // (128 * 513 * 4)
+    assert mla.mla_noalloc_scratch_bytes(rows_fit, 128) <= limit
+    assert mla.mla_noalloc_scratch_bytes(rows_fit + 1, 128) > limit
+    assert call(rows=rows_fit + 1) == -5
+    assert "scratch" in mla.mla_last_error()
+    assert call(out=None) == -1
+    assert call(out=vp(0x10008)) == -4
+    assert call(lo=vp(0x10002)) == -4
+    assert call(batch=0, rows=0) == 0
+    assert call(batch=-1) == -2
+
+
 def test_counters_reset():
     mla.mla_reset_counters()
     assert mla.mla_get_counters() == [0, 0, 0, 0]
