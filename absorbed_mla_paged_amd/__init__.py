@@ -29,6 +29,7 @@ STATUS = {0: "MLA_OK", -1: "MLA_E_NULL", -2: "MLA_E_SHAPE", -3: "MLA_E_RANGE",
 EXPORTS = ["mla_default_plan_params", "mla_choose_partitions", "mla_partition_range",
            "mla_decode_partition", "mla_decode_partition_fp8", "mla_decode_reduce",
            "mla_decode_fused", "mla_decode_noalloc", "mla_noalloc_scratch_bytes",
+           "mla_stream_read",
            "mla_absorb_query",
            "mla_unabsorb_output", "mla_status_string",
            "mla_last_error", "mla_get_counters", "mla_reset_counters"]
@@ -101,6 +102,8 @@ def load_library(path: str | None = None):
     lib.mla_decode_noalloc.restype = ctypes.c_int
     lib.mla_noalloc_scratch_bytes.argtypes = [i32, i32, i32]
     lib.mla_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    lib.mla_stream_read.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_uint32, vp]
+    lib.mla_stream_read.restype = ctypes.c_int
     for name in ("mla_absorb_query", "mla_unabsorb_output"):
         getattr(lib, name).argtypes = [vp, vp, vp, i32, i32, i32, vp]
         getattr(lib, name).restype = ctypes.c_int
@@ -427,6 +430,19 @@ def mla_decode_noalloc(q_absorbed, q_pe, ckv_cache, kpe_cache, block_table, cont
         B, H, Q, float(scale), _dtype_code(q_absorbed), _ptr(partitions), _ptr(splits),
         _ptr(row_indptr), int(total_rows), int(max_rows_per_req), int(heads_per_wg), _ptr(out),
         _ptr(lse2_out), _stream(stream)))
+
+
+def mla_stream_read(src, sink, stream=None):
+    """Measurement helper: one plain contiguous read of the bytes of `src`
+    (a contiguous device tensor of 16-byte multiple size); `sink` is a
+    device int32/uint32 tensor of at least one element that stays
+    untouched (see include/mla_decode.h)."""
+    lib = load_library()
+    if not src.is_contiguous() or sink.numel() < 1:
+        raise MlaError(-2, "src must be contiguous and sink non-empty")
+    _need_cuda(src, sink)
+    nbytes = src.numel() * src.element_size()
+    _check(lib.mla_stream_read(_ptr(src), nbytes, _ptr(sink), 0xA5A5A5A5, _stream(stream)))
 
 
 def fused_sync_errors(sync) -> int:

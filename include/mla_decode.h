@@ -410,6 +410,21 @@ int mla_decode_noalloc(const void* q_absorbed, const void* q_pe, const void* ckv
  * their LSEs (0 for negative arguments). */
 size_t mla_noalloc_scratch_bytes(int32_t total_rows, int32_t num_heads, int32_t q_len);
 
+/*
+ * mla_stream_read -- measurement helper, not part of the decode: one launch
+ * of a plain contiguous read of `bytes` bytes at `src` (4096 workgroups of
+ * 256 threads, one 16-byte load per thread and iteration). It is the
+ * reference a benchmark times over the same byte count as a partition
+ * launch, for the rate a launch that only reads reaches on this device.
+ * src         dev, 16-byte aligned; bytes a multiple of 16 (0: nothing)
+ * sink        dev uint32 [1]: written only if the XOR of the data read
+ *             equals `never` (pass a value the data cannot fold to), so the
+ *             loads stay and nothing is written in practice
+ * Errors: MLA_E_NULL, MLA_E_ALIGN, MLA_E_HIP.
+ */
+int mla_stream_read(const void* src, size_t bytes, uint32_t* sink, uint32_t never,
+                    hipStream_t stream);
+
 /* Text for a status code (static storage). */
 const char* mla_status_string(int status);
 

@@ -300,6 +300,17 @@ def test_decode_noalloc_host_checks_launch_nothing():
     assert call(batch=-1) == -2
 
 
+def test_stream_read_host_checks():
+    lib = mla.load_library()
+    vp = ctypes.c_void_p
+    g = vp(0x10000)
+    assert lib.mla_stream_read(None, 1024, g, 5, None) == -1
+    assert lib.mla_stream_read(g, 1024, None, 5, None) == -1
+    assert lib.mla_stream_read(vp(0x10008), 1024, g, 5, None) == -4
+    assert lib.mla_stream_read(g, 1000, g, 5, None) == -4
+    assert lib.mla_stream_read(None, 0, None, 5, None) == 0
+
+
 def test_counters_reset():
     mla.mla_reset_counters()
     assert mla.mla_get_counters() == [0, 0, 0, 0]
