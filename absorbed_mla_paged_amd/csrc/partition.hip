@@ -86,7 +86,7 @@ static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 // no argument fetch; the PartitionArgs block is fetched meanwhile.
 template <int DT, bool FUSED, int PG, bool KV8>
 __global__ __launch_bounds__(THREADS) void partition_kernel(
-    int32_t groups, int32_t rows_per_req, int32_t slots, int32_t flags, int32_t total_rows,
+    int32_t groups, int32_t batch, int32_t slots, int32_t flags, int32_t total_rows,
     int32_t max_blocks, const int32_t* __restrict__ context_lens,
     const int32_t* __restrict__ row_indptr, const int32_t* __restrict__ partitions,
     const int32_t* __restrict__ splits, const int32_t* __restrict__ block_table,
@@ -106,18 +106,12 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
   const bool copier = wave >= CWAVES;
   const int direct = flags & 1;
 
-  // ---- which (request, local row, head group) this workgroup owns -------
-  // Workgroups are dealt to the 8 XCDs round-robin by linear id. Row slot
-  // u = b * rows_per_req + x; the id layout L = ((u / 8) * G + hg) * 8 + u % 8
-  // keeps the G head groups of one row on one XCD, so they share its L2.
-  const int L = blockIdx.x;
-  const int sl = L >> 3;
-  const int hg = sl % groups;
-  const int u = (sl / groups) * 8 + (L & 7);
-  if (u >= slots) return;
-
-  const int b = u / rows_per_req;
-  const int x = u % rows_per_req;
+  // ---- which (request, row, head group) this workgroup owns -------------
+  // Slot u is the global row of a split launch (its request found in
+  // row_indptr) or the request of a single-pass one (slot_of).
+  int u, hg;
+  if (!slot_of(blockIdx.x, groups, slots, &u, &hg)) return;
+  const int b = direct ? u : request_of_row(row_indptr, batch, u);
 
   const int head0 = hg * HG;
   const int64_t qrow0 = (int64_t)b * a.heads + head0;   // first (b, head) row
@@ -136,7 +130,7 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
 
   // All row metadata in one round trip.
   int n = load_const(context_lens, b);
-  int P = 1, S = 1, row = b, nrows = 1;
+  int P = 1, S = 1, row = b, x = 0, nrows = 1;
   if (!direct) {
     const int r0 = load_const(row_indptr, b);
     const int r1 = load_const(row_indptr, b + 1);
@@ -145,10 +139,11 @@ __global__ __launch_bounds__(THREADS) void partition_kernel(
     nrows = r1 - r0;
     P = max(1, min(pv, 1 << 25));
     S = max(1, min(sv, 1 << 25));
-    row = r0 + x;
+    row = u;
+    x = u - r0;
   }
   n = max(0, min(n, max_blocks * PG));
-  if (x >= nrows || row < 0 || row >= total_rows) return;
+  if (x < 0 || x >= nrows || row < 0 || row >= total_rows) return;
   if constexpr (FUSED) {
     if (tid == 0)
       __hip_atomic_fetch_add(fh + fused::kStarted, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -741,20 +736,19 @@ int partition_launch(bool fused, bool kv8, float kv_scale, const void* q_absorbe
     a.out_scale = kv_scale;
   }
   const int32_t groups = qrows / hpw;
-  const int32_t rows_per_req = direct ? 1 : max_rows_per_req;
-
-  const int64_t slots = (int64_t)batch * rows_per_req;
+  // One slot per request (single pass) or per row (split): see slot_of.
+  const int64_t slots = direct ? batch : total_rows;
   const int64_t wgs = ((slots + 7) / 8) * 8 * groups;
   if (wgs > INT32_MAX || slots > INT32_MAX)
     return fail(MLA_E_SHAPE, "grid too large (%lld workgroups)", (long long)wgs);
   const dim3 grid((unsigned)wgs), block(THREADS);
   const int32_t dflag = part::pack_flags(direct, q_len, num_heads), sl = (int32_t)slots;
   if (hpw != HG)
-    part::launch_wide(dtype, block_size, kv8, (unsigned)wgs, stream, groups, rows_per_req, sl, dflag,
+    part::launch_wide(dtype, block_size, kv8, (unsigned)wgs, stream, groups, batch, sl, dflag,
                       total_rows, max_blocks_per_seq, context_lens, row_indptr, partitions,
                       splits, block_table, a);
 #define MLA_LAUNCH(K)                                                                        \
-  hipLaunchKernelGGL(K, grid, block, 0, stream, groups, rows_per_req, sl, dflag, total_rows, \
+  hipLaunchKernelGGL(K, grid, block, 0, stream, groups, batch, sl, dflag, total_rows, \
                      max_blocks_per_seq, context_lens, row_indptr, partitions, splits,       \
                      block_table, a)
   else if (kv8) {

@@ -85,20 +85,33 @@ struct RowInfo {
   int nseg;     // 32-token segments holding at least one visible token
 };
 
-// Which (request, local row, head group) workgroup L owns. Workgroups are
-// dealt to the 8 XCDs round-robin by linear id; slot u = b * rows_per_req +
-// x, and the id layout L = ((u / 8) * G + hg) * 8 + u % 8 keeps the G head
-// groups of one row on one XCD, so they share its L2. Returns false for a
-// workgroup with nothing to do (grid padding, or x past the request's rows).
-__device__ __forceinline__ bool slot_of(int L, int groups, int rows_per_req, int slots,
-                                        int* b, int* x, int* hg) {
+// Which row slot and head group workgroup L owns. Workgroups are dealt to
+// the 8 XCDs round-robin by linear id. Slot u is the global row index of a
+// split launch (request-major, so every XCD gets the same number of rows,
+// within one, whatever the requests' row counts), or the request of a
+// single-pass launch. The id layout L = ((u / 8) * G + hg) * 8 + u % 8
+// keeps the G head groups of one row on one XCD, so they share its L2.
+// Returns false for grid padding.
+__device__ __forceinline__ bool slot_of(int L, int groups, int slots, int* u, int* hg) {
   const int sl = L >> 3;
   *hg = sl % groups;
-  const int u = (sl / groups) * 8 + (L & 7);
-  if (u >= slots) return false;
-  *b = u / rows_per_req;
-  *x = u % rows_per_req;
-  return true;
+  *u = (sl / groups) * 8 + (L & 7);
+  return *u < slots;
+}
+
+// Request of global row r: the b in [0, batch) with row_indptr[b] <= r <
+// row_indptr[b + 1], by binary search over the (non-decreasing) row_indptr
+// with scalar loads; ceil(log2(batch)) dependent loads, none for one
+// request. A malformed row_indptr still yields some b in range, and the
+// caller's check of r against that request's rows then rejects the row.
+__device__ __forceinline__ int request_of_row(const int32_t* row_indptr, int batch, int r) {
+  int lo = 0, hi = batch;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (dev::load_const(row_indptr, mid) <= r) lo = mid;
+    else hi = mid;
+  }
+  return lo;
 }
 
 // Row metadata in one round of scalar loads, then the index math of
@@ -107,15 +120,18 @@ __device__ __forceinline__ bool slot_of(int L, int groups, int rows_per_req, int
 // cut from the whole context; `hidden` more tokens at its end are masked for
 // this head group (new token j of a window of q_len sees all but the last
 // q_len - 1 - j).
+// Slot u is request b (single pass) or global row u (split launch, request
+// found by request_of_row).
 template <int PG>
-__device__ __forceinline__ bool find_row(int b, int x, int direct, int total_rows, int hidden,
+__device__ __forceinline__ bool find_row(int u, int batch, int direct, int total_rows, int hidden,
                                          int max_blocks, const int32_t* context_lens,
                                          const int32_t* row_indptr,
                                          const int32_t* partitions, const int32_t* splits,
                                          RowInfo* ri) {
   using dev::load_const;
+  const int b = direct ? u : request_of_row(row_indptr, batch, u);
   int n = load_const(context_lens, b);
-  int P = 1, S = 1, row = b, nrows = 1;
+  int P = 1, S = 1, row = b, x = 0, nrows = 1;
   if (!direct) {
     const int r0 = load_const(row_indptr, b);
     const int r1 = load_const(row_indptr, b + 1);
@@ -124,10 +140,11 @@ __device__ __forceinline__ bool find_row(int b, int x, int direct, int total_row
     nrows = r1 - r0;
     P = max(1, min(pv, 1 << 25));
     S = max(1, min(sv, 1 << 25));
-    row = r0 + x;
+    row = u;
+    x = u - r0;
   }
   n = max(0, min(n, max_blocks * PG));
-  if (x >= nrows || row < 0 || row >= total_rows) return false;
+  if (x < 0 || x >= nrows || row < 0 || row >= total_rows) return false;
   const int p = x / S;
   const int s = x % S;
   const int nblk = cdiv(n, PG);
@@ -183,7 +200,7 @@ __device__ __forceinline__ void bump_counter(MLA_LDS uint32_t* c, int lane) {
 // Launch of the wide kernel (heads_per_wg 64); arguments as the 16-head
 // kernel's, kv8 for E4M3 caches. Host side, after the launcher's checks.
 void launch_wide(int dtype, int block_size, bool kv8, unsigned wgs, hipStream_t stream,
-                 int32_t groups, int32_t rows_per_req, int32_t slots, int32_t flags,
+                 int32_t groups, int32_t batch, int32_t slots, int32_t flags,
                  int32_t total_rows, int32_t max_blocks, const int32_t* context_lens,
                  const int32_t* row_indptr, const int32_t* partitions, const int32_t* splits,
                  const int32_t* block_table, const PartitionArgs& a);

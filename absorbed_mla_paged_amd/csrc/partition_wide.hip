@@ -169,7 +169,7 @@ __device__ __forceinline__ void meet() {
 // scale_log2 and out_scale).
 template <int DT, int PG, bool KV8>
 __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
-    int32_t groups, int32_t rows_per_req, int32_t slots, int32_t flags, int32_t total_rows,
+    int32_t groups, int32_t batch, int32_t slots, int32_t flags, int32_t total_rows,
     int32_t max_blocks, const int32_t* __restrict__ context_lens,
     const int32_t* __restrict__ row_indptr, const int32_t* __restrict__ partitions,
     const int32_t* __restrict__ splits, const int32_t* __restrict__ block_table,
@@ -195,15 +195,16 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
   const int hp = sw & 1;      // score waves: my 32 heads are 32 hp .. +32
   const int tt = sw >> 1;     // score waves: my 16 tokens are 16 tt .. +16
 
-  int b, x, hg;
-  if (!slot_of(blockIdx.x, groups, rows_per_req, slots, &b, &x, &hg)) return;
+  int u, hg;
+  if (!slot_of(blockIdx.x, groups, slots, &u, &hg)) return;
   const int hwg = hg * HPW;   // first head of the workgroup
 
   const int direct = flags & 1;
   RowInfo ri;
-  if (!find_row<PG>(b, x, direct, total_rows, hidden_tail(flags, hwg), max_blocks, context_lens,
-                row_indptr, partitions, splits, &ri))
+  if (!find_row<PG>(u, batch, direct, total_rows, hidden_tail(flags, hwg), max_blocks,
+                    context_lens, row_indptr, partitions, splits, &ri))
     return;
+  const int b = ri.b;
   const int row = ri.row;
   const int nblocks = ri.nseg;   // 32-token blocks of the row
   // Output of value-wave lane (ln, lg) for head tile ht (head hwg + 16 ht +
@@ -721,7 +722,7 @@ __global__ __launch_bounds__(THREADS, 1) void wide_kernel(
 }  // namespace
 
 void launch_wide(int dtype, int block_size, bool kv8, unsigned wgs, hipStream_t stream,
-                 int32_t groups, int32_t rows_per_req, int32_t slots, int32_t flags,
+                 int32_t groups, int32_t batch, int32_t slots, int32_t flags,
                  int32_t total_rows, int32_t max_blocks, const int32_t* context_lens,
                  const int32_t* row_indptr, const int32_t* partitions, const int32_t* splits,
                  const int32_t* block_table, const PartitionArgs& a) {
@@ -734,7 +735,7 @@ void launch_wide(int dtype, int block_size, bool kv8, unsigned wgs, hipStream_t 
     kernel = dtype == MLA_F16
                  ? (block_size == 16 ? wide_kernel<0, 16, false> : wide_kernel<0, 32, false>)
                  : (block_size == 16 ? wide_kernel<1, 16, false> : wide_kernel<1, 32, false>);
-  hipLaunchKernelGGL(kernel, dim3(wgs), dim3(THREADS), 0, stream, groups, rows_per_req, slots,
+  hipLaunchKernelGGL(kernel, dim3(wgs), dim3(THREADS), 0, stream, groups, batch, slots,
                      flags, total_rows, max_blocks, context_lens, row_indptr, partitions, splits,
                      block_table, a);
 }
