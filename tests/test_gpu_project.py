@@ -39,7 +39,7 @@ def host(t):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("rows,heads", [(1, 16), (3, 16), (8, 128), (13, 128), (2, 48)])
+@pytest.mark.parametrize("rows,heads", [(1, 16), (3, 16), (8, 128), (13, 128), (2, 48), (17, 128), (40, 16)])
 def test_fold_and_unfold_match_oracle(dtype, rows, heads):
     import torch
     rng = np.random.default_rng(rows * 1000 + heads)
