@@ -9,17 +9,20 @@
 // "How #898's merge kernel is reused"; zero weight for rows with no visible
 // key and a single rounding after the merge per MTPLX pull request 639.)
 //
-// One workgroup handles (b, h, a slice of 32 or 64 dims): 256 threads as
-// row lanes x (slice / 4) threads, each thread owning 4 consecutive dims
-// (one 16-byte load per row), so a row's slice is one 128- or 256-byte
-// piece. Row lane k takes rows k, k + RL, ... in order, with 8 rows' loads
+// One workgroup handles (b, h, a slice of 32, 64 or 256 dims): 256 threads
+// as row lanes x (slice / 4) threads, each thread owning 4 consecutive dims
+// (one 16-byte load per row), so a row's slice is one 128-, 256- or
+// 1024-byte piece. Row lane k takes rows k, k + RL, ... in order, with 8 rows' loads
 // (slice and lse2) issued before any is used, so a request's whole partial
 // set is in flight at once, in a single round trip. Each row lane keeps its
 // own running maximum, weighted sum and weight; the row lanes are then
 // merged in a fixed tree order (lane shuffles, then the four waves), so the
 // result is bit-identical run to run. The launch takes 64-dim slices when
 // that still gives at least 1024 workgroups (many heads: fewer, wider
-// workgroups), else 32-dim ones (16 heads: more workgroups in flight).
+// workgroups), else 32-dim ones (16 heads: more workgroups in flight); and
+// 256-dim slices when requests have 32 rows or fewer on average (a batch of
+// many requests: 4 row lanes x 8 rows hold them, and far fewer workgroups
+// of mostly idle lanes are launched).
 #include "device_common.h"
 #include "internal.h"
 
@@ -34,6 +37,10 @@ constexpr int LAT = MLA_KV_LORA_RANK;
 constexpr int THREADS = 256;
 constexpr int UNROLL = 8;                 // rows in flight per thread
 constexpr int WIDE_MIN_WGS = 1024;        // 64-dim slices from this many workgroups
+// Requests of at most this many rows on average (all of them one load batch
+// of 4 row lanes x 8) take 256-dim slices: 4 waves, one row lane each.
+constexpr int FEW_ROWS = 32;
+constexpr int FEW_ROWS_MIN_WGS = 256;
 
 struct ReduceArgs {
   const float* partial_out;
@@ -51,7 +58,7 @@ __global__ __launch_bounds__(THREADS) void reduce_kernel(ReduceArgs a) {
   constexpr int SLICES = LAT / SLICE;     // workgroups per (request, head)
   constexpr int TPR = SLICE / 4;          // threads per row
   constexpr int RL = THREADS / TPR;       // row lanes
-  static_assert(SLICE == 32 || SLICE == 64, "slice width");
+  static_assert(SLICE == 32 || SLICE == 64 || SLICE == 256, "slice width");
   typedef Elem<DT> E;
   __shared__ f32x4 part[THREADS / 64][TPR];
   __shared__ float lane_m[THREADS / 64], lane_w[THREADS / 64];
@@ -188,7 +195,10 @@ extern "C" int mla_decode_reduce(const float* partial_out, const float* partial_
       (lse2_out && !aligned(lse2_out, 4)))
     return fail(MLA_E_ALIGN, "misaligned buffer");
   const bool wide = (int64_t)batch * num_heads * (LAT / 64) >= WIDE_MIN_WGS;
-  const int64_t wgs = (int64_t)batch * num_heads * (LAT / (wide ? 64 : 32));
+  const bool few = total_rows <= (int64_t)FEW_ROWS * batch &&
+                   (int64_t)batch * num_heads * (LAT / 256) >= FEW_ROWS_MIN_WGS;
+  const int slice = few ? 256 : wide ? 64 : 32;
+  const int64_t wgs = (int64_t)batch * num_heads * (LAT / slice);
   if (wgs > INT32_MAX) return fail(MLA_E_SHAPE, "grid too large");
   ReduceArgs a;
   a.partial_out = partial_out;
@@ -199,8 +209,9 @@ extern "C" int mla_decode_reduce(const float* partial_out, const float* partial_
   a.batch = batch;
   a.heads = num_heads;
   a.total_rows = total_rows;
-  auto kernel = dtype == MLA_F16 ? (wide ? reduce_kernel<0, 64> : reduce_kernel<0, 32>)
-                                 : (wide ? reduce_kernel<1, 64> : reduce_kernel<1, 32>);
+  auto kernel = dtype == MLA_F16
+                    ? (few ? reduce_kernel<0, 256> : wide ? reduce_kernel<0, 64> : reduce_kernel<0, 32>)
+                    : (few ? reduce_kernel<1, 256> : wide ? reduce_kernel<1, 64> : reduce_kernel<1, 32>);
   hipLaunchKernelGGL(kernel, dim3((unsigned)wgs), dim3(THREADS), 0, stream, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(MLA_E_HIP, "reduce launch: %s", hipGetErrorString(e));
