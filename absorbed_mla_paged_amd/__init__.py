@@ -29,7 +29,7 @@ STATUS = {0: "MLA_OK", -1: "MLA_E_NULL", -2: "MLA_E_SHAPE", -3: "MLA_E_RANGE",
 EXPORTS = ["mla_default_plan_params", "mla_choose_partitions", "mla_partition_range",
            "mla_decode_partition", "mla_decode_partition_fp8", "mla_decode_reduce",
            "mla_decode_fused", "mla_decode_noalloc", "mla_noalloc_scratch_bytes",
-           "mla_stream_read",
+           "mla_stream_read", "mla_copy_probe",
            "mla_absorb_query",
            "mla_unabsorb_output", "mla_status_string",
            "mla_last_error", "mla_get_counters", "mla_reset_counters"]
@@ -102,6 +102,8 @@ def load_library(path: str | None = None):
     lib.mla_decode_noalloc.restype = ctypes.c_int
     lib.mla_noalloc_scratch_bytes.argtypes = [i32, i32, i32]
     lib.mla_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    lib.mla_copy_probe.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, i32, vp]
+    lib.mla_copy_probe.restype = ctypes.c_int
     lib.mla_stream_read.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_uint32, vp]
     lib.mla_stream_read.restype = ctypes.c_int
     for name in ("mla_absorb_query", "mla_unabsorb_output"):
@@ -443,6 +445,23 @@ def mla_stream_read(src, sink, stream=None):
     _need_cuda(src, sink)
     nbytes = src.numel() * src.element_size()
     _check(lib.mla_stream_read(_ptr(src), nbytes, _ptr(sink), 0xA5A5A5A5, _stream(stream)))
+
+
+def mla_copy_probe(ckv_cache, kpe_cache, table, rows: int, blocks_per_row: int, groups: int,
+                   waves: int = 8, inflight: int = 8, stream=None):
+    """Measurement helper: copy paged rows' KV into LDS only (see
+    include/mla_decode.h); `table` is an int32 device tensor of
+    rows * blocks_per_row block indices."""
+    import torch
+    lib = load_library()
+    _tensor(ckv_cache, "ckv_cache", _f16_types(), shape=(None, BLOCK_SIZE, KV_LORA_RANK))
+    _tensor(kpe_cache, "kpe_cache", (ckv_cache.dtype,),
+            shape=(int(ckv_cache.shape[0]), BLOCK_SIZE, ROPE_DIM))
+    _tensor(table, "table", (torch.int32,), numel=int(rows) * int(blocks_per_row))
+    _need_cuda(ckv_cache, kpe_cache, table)
+    _check(lib.mla_copy_probe(_ptr(ckv_cache), _ptr(kpe_cache), int(ckv_cache.shape[0]),
+                              _ptr(table), int(rows), int(blocks_per_row), int(groups),
+                              int(waves), int(inflight), _stream(stream)))
 
 
 def fused_sync_errors(sync) -> int:

@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla_decode.so")
 SOURCES = ["plan.cpp", "partition.hip", "partition_wide.hip", "reduce.hip", "project.hip",
-           "noalloc.hip", "stream_read.hip"]
+           "noalloc.hip", "stream_read.hip", "copy_probe.hip"]
 HEADERS = ["internal.h", "device_common.h", "partition_common.h", "fused_common.h"]
 # Per-source extra flags (none needed at present).
 EXTRA: dict[str, list[str]] = {}

@@ -425,6 +425,25 @@ size_t mla_noalloc_scratch_bytes(int32_t total_rows, int32_t num_heads, int32_t 
 int mla_stream_read(const void* src, size_t bytes, uint32_t* sink, uint32_t never,
                     hipStream_t stream);
 
+/*
+ * mla_copy_probe -- measurement helper, not part of the decode: one launch
+ * that only copies the KV of paged rows into LDS, as the partition kernels'
+ * copies do (global_load_lds_dwordx4, 1 KB per instruction: the 32 ckv rows
+ * and 4 kpe pieces of each 32-token block), with `groups` workgroups per
+ * row on one XCD (1: every block read by one CU; 2 or 4: by that many, as
+ * the 64-head workgroups of a 128-head row read it), `waves` copying waves
+ * (4 or 8) each keeping `inflight` copies (4, 8 or 16) in flight. It shows
+ * the rate the memory path gives such copies apart from any arithmetic.
+ * ckv_pool   dev 16-bit [num_blocks, 32, 512]; kpe_pool dev 16-bit
+ *            [num_blocks, 32, 64]
+ * table      dev int32 [rows, blocks_per_row]: block k of row u is
+ *            table[u * blocks_per_row + k] (clamped into [0, num_blocks))
+ * Errors: MLA_E_NULL, MLA_E_SHAPE, MLA_E_UNSUPPORTED, MLA_E_HIP.
+ */
+int mla_copy_probe(const void* ckv_pool, const void* kpe_pool, int32_t num_blocks,
+                   const int32_t* table, int32_t rows, int32_t blocks_per_row, int32_t groups,
+                   int32_t waves, int32_t inflight, hipStream_t stream);
+
 /* Text for a status code (static storage). */
 const char* mla_status_string(int status);
 

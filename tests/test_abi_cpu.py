@@ -311,6 +311,17 @@ def test_stream_read_host_checks():
     assert lib.mla_stream_read(None, 0, None, 5, None) == 0
 
 
+def test_copy_probe_host_checks():
+    lib = mla.load_library()
+    vp = ctypes.c_void_p
+    g = vp(0x10000)
+    assert lib.mla_copy_probe(None, g, 8, g, 2, 4, 1, 8, 8, None) == -1
+    assert lib.mla_copy_probe(g, g, 8, g, 0, 4, 1, 8, 8, None) == -2
+    assert lib.mla_copy_probe(g, g, 8, g, 2, 4, 3, 8, 8, None) == -2
+    assert lib.mla_copy_probe(g, g, 8, g, 2, 4, 1, 6, 8, None) == -6
+    assert lib.mla_copy_probe(g, g, 8, g, 2, 4, 1, 8, 32, None) == -6
+
+
 def test_counters_reset():
     mla.mla_reset_counters()
     assert mla.mla_get_counters() == [0, 0, 0, 0]
