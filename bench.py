@@ -57,19 +57,23 @@ FETCH_SCALE = 2.0
 WRITE_SCALE = 1.0
 MEASURED = {
     # profiles/partition_kernel_v2lite_32k.md
-    ("v2lite_32k", "62a2d525416b"): dict(fetch_kib=18631.7, write_kib=8208.0, mfma_busy=0.022),
-    ("v2lite_32k@bs16", "62a2d525416b"): dict(fetch_kib=18633.7, write_kib=8208.0,
+    ("v2lite_32k", "cf90aa654a53"): dict(fetch_kib=18630.2, write_kib=8208.0, mfma_busy=0.022),
+    ("v2lite_32k@bs16", "cf90aa654a53"): dict(fetch_kib=18635.3, write_kib=8208.0,
                                               mfma_busy=0.022),
+    ("two_req_32k_32k", "cf90aa654a53"): dict(fetch_kib=37134.5, write_kib=8208.0,
+                                              mfma_busy=0.034),
     # profiles/partition_kernel_v2lite_32k_fp8.md
-    ("v2lite_32k@fp8_e4m3", "62a2d525416b"): dict(fetch_kib=9426.6, write_kib=8208.0,
+    ("v2lite_32k@fp8_e4m3", "cf90aa654a53"): dict(fetch_kib=9426.6, write_kib=8208.0,
                                                   mfma_busy=0.024),
     # profiles/wide_kernel_v3_131k.md
-    ("v3_131k", "2ee7e513cb59"): dict(fetch_kib=74502.2, write_kib=32832.0, mfma_busy=0.285),
+    ("v3_131k", "42ccfc983e44"): dict(fetch_kib=74501.3, write_kib=32832.0, mfma_busy=0.286),
     # profiles/wide_kernel_v3_81k.md
-    ("v3_81k", "2ee7e513cb59"): dict(fetch_kib=46882.6, write_kib=32062.5, mfma_busy=0.232),
+    ("v3_81k", "42ccfc983e44"): dict(fetch_kib=46884.2, write_kib=32062.5, mfma_busy=0.230),
+    # profiles/wide_kernel_mixed_b8.md
+    ("mixed_b8", "42ccfc983e44"): dict(fetch_kib=326796.0, write_kib=32062.5, mfma_busy=0.348),
     # profiles/wide_kernel_v3_131k_fp8.md
-    ("v3_131k@fp8_e4m3", "2ee7e513cb59"): dict(fetch_kib=37626.7, write_kib=32832.0,
-                                               mfma_busy=0.274),
+    ("v3_131k@fp8_e4m3", "42ccfc983e44"): dict(fetch_kib=37628.3, write_kib=32832.0,
+                                               mfma_busy=0.276),
 }
 
 
