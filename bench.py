@@ -514,6 +514,11 @@ def measure(label, name, prm_kw, args, torch, mla, stream, sref, cpu_budget):
         "partition_us": round(part_us, 3),
         "reduce_us": round(reduce_us, 3) if reduce_us else None,
         "achieved_gbs_pair": round(pair_gbs, 1),
+        # the whole step (algorithmic bytes of the call over the step time)
+        # against the 8 TB/s peak and against the plain read of the
+        # partition's bytes
+        "pair_frac": round(pair_gbs / HBM_PEAK_GBS, 4),
+        "pair_frac_of_stream": round(pair_gbs / stream_gbs, 4) if stream_gbs else None,
         "split_bytes_written": split_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -531,6 +536,11 @@ def measure(label, name, prm_kw, args, torch, mla, stream, sref, cpu_budget):
                      # re-reads worth chasing
                      "traffic_vs_algorithmic": (round(traffic / (alg["partition"] + part_written), 3)
                                                 if traffic else None),
+                     # counted HBM traffic over the launch time, and whether
+                     # it exceeds the bytes the launch must move by over 10%
+                     "traffic_gbs": round(traffic / (part_us * 1e-6) / 1e9, 1) if traffic else None,
+                     "traffic_excess_flag": (traffic > 1.10 * (alg["partition"] + part_written)
+                                             if traffic else None),
                      # FETCH_SIZE and WRITE_SIZE as read (KiB per dispatch),
                      # and the scale factors applied to them (the copy
                      # calibration: FETCH_SIZE reads half of a known copy)
