@@ -438,7 +438,9 @@ def mla_stream_read(src, sink, stream=None):
     """Measurement helper: one plain contiguous read of the bytes of `src`
     (a contiguous device tensor of 16-byte multiple size); `sink` is a
     device int32/uint32 tensor of at least one element that stays
-    untouched (see include/mla_decode.h)."""
+    untouched as long as no thread's XOR fold of the words it reads is
+    0xA5A5A5A5: data whose 4-byte words all keep bit 31 clear qualifies
+    (see include/mla_decode.h)."""
     lib = load_library()
     if not src.is_contiguous() or sink.numel() < 1:
         raise MlaError(-2, "src must be contiguous and sink non-empty")

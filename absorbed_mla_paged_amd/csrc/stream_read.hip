@@ -7,9 +7,10 @@
 // 4096 workgroups of 256 threads (16 per CU) stride through the buffer with
 // one 16-byte load per thread and iteration: the launch shape that read
 // fastest among 256..4096 workgroups and 1..4 loads per iteration at
-// 40-600 MB on MI355X. The loaded words are folded with XOR and stored only
-// if the fold equals a value the caller passes and the data never holds, so
-// the loads cannot be dropped and nothing is written.
+// 40-600 MB on MI355X. Each thread folds the words it loaded with XOR and
+// stores the fold only if it equals a value the caller passes and no fold
+// of the data can take, so the loads cannot be dropped and nothing is
+// written.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"

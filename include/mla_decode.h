@@ -417,9 +417,10 @@ size_t mla_noalloc_scratch_bytes(int32_t total_rows, int32_t num_heads, int32_t 
  * reference a benchmark times over the same byte count as a partition
  * launch, for the rate a launch that only reads reaches on this device.
  * src         dev, 16-byte aligned; bytes a multiple of 16 (0: nothing)
- * sink        dev uint32 [1]: written only if the XOR of the data read
- *             equals `never` (pass a value the data cannot fold to), so the
- *             loads stay and nothing is written in practice
+ * sink        dev uint32 [1]: written only by a thread whose XOR fold of
+ *             the 4-byte words it read equals `never` (pass a value no such
+ *             fold can take, e.g. one with a bit set that no word of the
+ *             data has), so the loads stay and nothing is written
  * Errors: MLA_E_NULL, MLA_E_ALIGN, MLA_E_HIP.
  */
 int mla_stream_read(const void* src, size_t bytes, uint32_t* sink, uint32_t never,
