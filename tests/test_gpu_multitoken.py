@@ -67,6 +67,8 @@ EDGE = [
     ([31, 4000], 64, "f16", 3, {}),                          # 64-head workgroups
     ([5000], 128, "bf16", 2, dict(force_partitions=3, force_splits=2)),
     ([64], 16, "bf16", 8, dict(force_partitions=2, force_splits=2)),   # window = the last block
+    ([3000], 128, "bf16", 8, {}),                            # the largest window: 1024 query rows
+    ([1500, 700], 128, "f16", 8, dict(heads_per_wg=16)),     # the same in 16-head workgroups
 ]
 
 
