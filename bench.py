@@ -715,6 +715,8 @@ def main():
         "partition_us": head["partition_us"],
         "reduce_us": head["reduce_us"],
         "achieved_gbs_pair": head["achieved_gbs_pair"],
+        "pair_frac": head["pair_frac"],
+        "pair_frac_of_stream": head["pair_frac_of_stream"],
         "roofline": head["roofline"],
         "cpu_baseline": head["cpu_baseline"],
         "host": platform.node(),
