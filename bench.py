@@ -539,6 +539,10 @@ def measure(label, name, prm_kw, args, torch, mla, stream, sref, cpu_budget):
                      # counted HBM traffic over the launch time, and whether
                      # it exceeds the bytes the launch must move by over 10%
                      "traffic_gbs": round(traffic / (part_us * 1e-6) / 1e9, 1) if traffic else None,
+                     "traffic_frac": (round(traffic / (part_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                                      if traffic else None),
+                     "traffic_frac_of_stream": (round(traffic / (part_us * 1e-6) / 1e9 / stream_gbs, 4)
+                                                if traffic and stream_gbs else None),
                      "traffic_excess_flag": (traffic > 1.10 * (alg["partition"] + part_written)
                                              if traffic else None),
                      # FETCH_SIZE and WRITE_SIZE as read (KiB per dispatch),
